@@ -1,0 +1,243 @@
+"""Benchmark of the SparseLoCo hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic 8192 x 28672 fp32
+pseudo-gradient (Student-t(3) values, 20% exactly-zero chunks):
+  sl_compress     error feedback + top-64/4096 + 2-bit codes + 12-bit pack
+  sl_aggregate    decode and sum 24 peers' records into a dense fp32 update
+  sl_apply_mean   theta <- theta - sum / 24
+Inputs are resident in HBM before timing starts.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X published HBM3E bandwidth
+N_PEERS = 24
+BETA = 0.95
+CHUNK = 4096
+RECORD = 112 + 4                 # payload bytes + fp32 scale per chunk
+
+# Algorithmic bytes per parameter (what the method must move).
+BYTES_COMPRESS = 4 + 4 + 4 + RECORD / CHUNK           # read delta, ef; write ef; record
+BYTES_AGGREGATE = 4 + N_PEERS * RECORD / CHUNK        # write out; read 24 records
+BYTES_APPLY = 4 + 4 + 4                               # read theta, out; write theta
+
+METRIC = "compressed Gparams/s and % of HBM roofline (compress + 24-peer aggregate)"
+PROFILE = os.path.join(ROOT, "profiles", "compress_mlp_8192x28672_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "communication_efficient_distributed_amd", "csrc", "compress.hip")
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(n_params: int):
+    """HBM bytes per compress launch from the committed counter summary, or None
+    if there is none or it was taken on a different compress.hip."""
+    if not os.path.exists(PROFILE):
+        return None
+    txt = open(PROFILE).read()
+    m = re.search(r"compress_source_sha256_16:\s*([0-9a-f]{16})", txt)
+    if not m or m.group(1) != source_hash(KERNEL_SOURCE):
+        return None
+    f = re.search(r"compress_hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    p = re.search(r"params_per_launch:\s*(\d+)", txt)
+    if not f or not p or int(p.group(1)) != n_params:
+        return None
+    return float(f.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-chunks", type=int, default=8192)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a torch copy of 1 GiB (for counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only (the compressor and aggregator are "
+              "chunk-local; see the sharding notes in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import communication_efficient_distributed_amd as sl
+    from communication_efficient_distributed_amd import datagen
+
+    sl.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = datagen.MLP_8192x28672
+    n = datagen.WORKLOAD_PARAMS[W]
+    C = n // CHUNK
+
+    # Resident inputs.
+    delta = datagen.student_t3(n, W, 0, 0, dev)
+    ef = torch.zeros(n, dtype=torch.float32, device=dev)
+    payload = torch.empty((C, 112), dtype=torch.uint8, device=dev)
+    scales = torch.empty(C, dtype=torch.float32, device=dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    theta = datagen.theta0(n, W, dev)
+    peer_p, peer_s = [], []
+    scratch_ef = torch.zeros(n, dtype=torch.float32, device=dev)
+    for p in range(1, N_PEERS + 1):
+        d = datagen.student_t3(n, W, p, 0, dev)
+        scratch_ef.zero_()
+        pl, s = sl.compress(d, scratch_ef, BETA)
+        peer_p.append(pl)
+        peer_s.append(s)
+        del d
+    del scratch_ef
+    torch.cuda.synchronize()
+    # Copies kept for the CPU baseline (host side, first sample chunks).
+    ef0_host = ef.cpu().numpy()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sl.sl_compress(delta, ef, BETA, payload, scales)
+        if ev is not None:
+            ev[1].record(stream)
+        sl.sl_aggregate(peer_p, peer_s, out)
+        if ev is not None:
+            ev[2].record(stream)
+        sl.sl_apply_mean(theta, out, N_PEERS)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t_c = [e[0].elapsed_time(e[1]) for e in evs]
+    t_a = [e[1].elapsed_time(e[2]) for e in evs]
+    t_m = [e[2].elapsed_time(e[3]) for e in evs]
+    span_ms = evs[0][0].elapsed_time(evs[-1][3])
+    ms_per_step = span_ms / K
+    avg = lambda xs: float(sum(xs) / len(xs))
+    tc, ta, tm = avg(t_c), avg(t_a), avg(t_m)
+
+    def kstats(t_ms, bpp):
+        gps = n / (t_ms * 1e-3) / 1e9
+        gbs = bpp * n / (t_ms * 1e-3) / 1e9
+        return {"ms": round(t_ms, 5), "gparams_per_s": round(gps, 2), "gb_per_s": round(gbs, 1),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_param": round(bpp, 4)}
+
+    value = n / (ms_per_step * 1e-3) / 1e9
+    comp = kstats(tc, BYTES_COMPRESS)
+    traffic = traffic_from_profile(n)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "mlp_8192x28672_student_t3_zero20",
+            "params": n,
+            "chunks": C,
+            "peers": N_PEERS,
+            "beta": BETA,
+            "step": "sl_compress + sl_aggregate(24 peers) + sl_apply_mean",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "compress_kernel",
+            "achieved": comp["gb_per_s"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": comp["hbm_frac"],
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": round(BYTES_COMPRESS * n),
+        },
+        "kernels": {
+            "compress": comp,
+            "aggregate": kstats(ta, BYTES_AGGREGATE),
+            "apply_mean": kstats(tm, BYTES_APPLY),
+            "compress_plus_aggregate": kstats(tc + ta, BYTES_COMPRESS + BYTES_AGGREGATE),
+        },
+        "wall_s_timed": round(wall, 4),
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
+    """The CPU oracle on the first S chunks of the same workload, all host
+    threads, same three steps.  Reported as a baseline, not a target."""
+    import numpy as np
+
+    import oracle
+
+    S = min(args.cpu_sample_chunks, n // CHUNK)
+    m = S * CHUNK
+    d = delta[:m].cpu().numpy()
+    e = ef0_host[:m].copy()
+    pp = [p[:S].cpu().numpy() for p in peer_p]
+    ps = [s[:S].cpu().numpy() for s in peer_s]
+    th = theta[:m].cpu().numpy()
+    T = max(1, min(64, os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.compress(d, e, beta=BETA, nthreads=T, inplace=True)
+    agg = oracle.aggregate(pp, ps, m, nthreads=T)
+    oracle.apply_mean(th, agg, N_PEERS)
+    dt = time.perf_counter() - t0
+    return {"value": round(m / dt / 1e9, 5), "unit": "Gparams/s", "cores": T, "kind": "oracle",
+            "sample": f"first {S} chunks ({m} params) of the same workload: compress + "
+                      f"aggregate {N_PEERS} peers + apply_mean, {dt:.2f} s wall on {T} threads"}
+
+
+if __name__ == "__main__":
+    main()

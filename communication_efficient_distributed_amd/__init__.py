@@ -1,9 +1,24 @@
 """SparseLoCo pseudo-gradient compressor and aggregator for MI355X (gfx950).
 
-The compute path is the HIP library libsparseloco.so (C-ABI in
-include/sparseloco.h); the functions re-exported here marshal torch tensors
-into that library and do no arithmetic of their own.
+The compute path is the HIP library libsparseloco.so (C ABI in
+include/sparseloco.h).  The functions re-exported here marshal torch device
+tensors into that library and do no arithmetic of their own; they raise if the
+library is not built.
 """
 from . import datagen  # noqa: F401  (distributions only)
-
-__all__ = ["datagen"]
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    SL_CHUNK,
+    SL_MAX_PEERS,
+    SL_PAYLOAD_BYTES,
+    SL_TOPK,
+    LibraryMissing,
+    SparseLoCoError,
+    aggregate,
+    compress,
+    load,
+    sl_aggregate,
+    sl_apply_mean,
+    sl_compress,
+    sl_status_string,
+)

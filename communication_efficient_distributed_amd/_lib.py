@@ -1,0 +1,165 @@
+"""ctypes binding of libsparseloco.so (declared in include/sparseloco.h).
+
+Marshalling only: every function here passes device pointers, sizes and the
+current HIP stream to the library and raises on a non-OK status.  There is no
+fallback: if the library is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparseloco.so")
+
+SL_CHUNK = 4096
+SL_TOPK = 64
+SL_PAYLOAD_BYTES = 112
+SL_MAX_PEERS = 128
+
+STATUS = {
+    0: "SL_OK",
+    1: "SL_ERR_INVALID_ARG",
+    2: "SL_ERR_SHAPE",
+    3: "SL_ERR_ALIGN",
+    4: "SL_ERR_TOO_MANY_PEERS",
+    5: "SL_ERR_HIP",
+}
+
+EXPORTS = ("sl_compress", "sl_aggregate", "sl_apply_mean", "sl_status_string")
+
+
+class SparseLoCoError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {text}")
+        self.status = status
+
+
+class LibraryMissing(ImportError):
+    pass
+
+
+_handle = None
+
+
+def load():
+    """Load libsparseloco.so once; raise LibraryMissing if it is not built."""
+    global _handle
+    if _handle is not None:
+        return _handle
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    L.sl_compress.argtypes = [P, P, F32, P, P, I64, P]
+    L.sl_compress.restype = ctypes.c_int
+    L.sl_aggregate.argtypes = [P, P, I32, P, I64, P]
+    L.sl_aggregate.restype = ctypes.c_int
+    L.sl_apply_mean.argtypes = [P, P, I32, I64, P]
+    L.sl_apply_mean.restype = ctypes.c_int
+    L.sl_status_string.argtypes = [ctypes.c_int]
+    L.sl_status_string.restype = ctypes.c_char_p
+    _handle = L
+    return L
+
+
+def sl_status_string(status: int) -> str:
+    return load().sl_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SparseLoCoError(fn, status, sl_status_string(status))
+
+
+def _stream_of(t: torch.Tensor, stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def sl_compress(delta: torch.Tensor, ef: torch.Tensor, beta: float, payload: torch.Tensor,
+                scales: torch.Tensor, stream=None) -> None:
+    """One compression round: ef updated in place, payload [C,112] uint8 and
+    scales [C] float32 written.  Asynchronous on `stream` (default: current)."""
+    n = delta.numel()
+    if ef.numel() != n:
+        raise ValueError("delta and ef sizes differ")
+    C = n // SL_CHUNK
+    if payload.numel() != C * SL_PAYLOAD_BYTES or scales.numel() != C:
+        raise ValueError("payload must hold n/4096*112 bytes and scales n/4096 floats")
+    args = (_dev(delta, "delta", torch.float32), _dev(ef, "ef", torch.float32),
+            ctypes.c_float(beta), _dev(payload, "payload", torch.uint8),
+            _dev(scales, "scales", torch.float32), ctypes.c_int64(n), _stream_of(delta, stream))
+    with torch.cuda.device(delta.device):
+        _check("sl_compress", load().sl_compress(*args))
+
+
+def sl_aggregate(payloads, scales, out: torch.Tensor, stream=None) -> None:
+    """out[n] = sum over peers (in list order) of the decoded payloads."""
+    n = out.numel()
+    C = n // SL_CHUNK
+    if len(payloads) != len(scales):
+        raise ValueError("payloads and scales lists differ in length")
+    N = len(payloads)
+    pp = (ctypes.c_void_p * max(N, 1))()
+    sp = (ctypes.c_void_p * max(N, 1))()
+    for p in range(N):
+        if payloads[p].numel() != C * SL_PAYLOAD_BYTES or scales[p].numel() != C:
+            raise ValueError(f"peer {p}: payload/scales size does not match out")
+        pp[p] = _dev(payloads[p], f"payloads[{p}]", torch.uint8).value
+        sp[p] = _dev(scales[p], f"scales[{p}]", torch.float32).value
+    o = _dev(out, "out", torch.float32)
+    with torch.cuda.device(out.device):
+        _check("sl_aggregate", load().sl_aggregate(ctypes.cast(pp, ctypes.c_void_p),
+                                                   ctypes.cast(sp, ctypes.c_void_p),
+                                                   ctypes.c_int32(N), o, ctypes.c_int64(n),
+                                                   _stream_of(out, stream)))
+
+
+def sl_apply_mean(theta: torch.Tensor, out: torch.Tensor, n_peers: int, stream=None) -> None:
+    """theta <- theta - out / n_peers (in place)."""
+    n = theta.numel()
+    if out.numel() != n:
+        raise ValueError("theta and out sizes differ")
+    args = (_dev(theta, "theta", torch.float32), _dev(out, "out", torch.float32),
+            ctypes.c_int32(n_peers), ctypes.c_int64(n), _stream_of(theta, stream))
+    with torch.cuda.device(theta.device):
+        _check("sl_apply_mean", load().sl_apply_mean(*args))
+
+
+# Convenience wrappers that allocate outputs with torch (device memory only).
+
+def compress(delta: torch.Tensor, ef: torch.Tensor, beta: float = 0.95, stream=None):
+    C = delta.numel() // SL_CHUNK
+    payload = torch.empty((C, SL_PAYLOAD_BYTES), dtype=torch.uint8, device=delta.device)
+    scales = torch.empty(C, dtype=torch.float32, device=delta.device)
+    sl_compress(delta, ef, beta, payload, scales, stream)
+    return payload, scales
+
+
+def aggregate(payloads, scales, n: int | None = None, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    if out is None:
+        if n is None:
+            n = payloads[0].numel() // SL_PAYLOAD_BYTES * SL_CHUNK
+        dev = payloads[0].device if payloads else torch.device("cuda")
+        out = torch.empty(n, dtype=torch.float32, device=dev)
+    sl_aggregate(payloads, scales, out, stream)
+    return out

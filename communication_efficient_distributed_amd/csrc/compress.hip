@@ -1,0 +1,417 @@
+// compress.hip -- the SparseLoCo compressor kernel for gfx950.
+//
+// One pass over each 4096-parameter chunk ("The Sparse Frontier: SparseLoCo and
+// the Compression Math Behind Permissionless Pre-Training", section "SparseLoCo:
+// Three Compression Levers in One Pass"): error-feedback update, top-64 by
+// |value|, per-chunk scale with four 2-bit levels, 12-bit indices packed into a
+// 112-byte record, and the residual written back to the error-feedback buffer
+// (same page, "Why Extreme Sparsity Doesn't Break Convergence").
+//
+// Mapping: one 64-lane wavefront owns one chunk.  Lane l holds elements
+// 256*m + 4*l + j (m = 0..15, j = 0..3) in registers, so every global load and
+// store instruction of the wavefront touches one contiguous KiB.  The wavefront
+// has a private 8 KiB LDS slice; no barrier ties wavefronts together.
+//
+// Selection (exact, deterministic): find the 64th element of the order
+// (|acc| descending, index ascending) -- the "cut" -- by an MSB-first radix
+// select over the 31-bit magnitude key bits(acc) & 0x7fffffff:
+//   level 0  2048-bin LDS histogram of key bits 30..20 (exponent + 3 mantissa
+//            bits).  Exact zeros are counted with ballots instead of atomics.
+//   then     if the boundary bin holds exactly the entries still needed, the
+//            cut is "key >= bin start"; if it holds at most 64 entries, they
+//            are compacted to LDS and ranked exactly by (key, index) with
+//            cross-lane reads; otherwise refine with 1024-bin histograms of
+//            key bits 19..10 and 9..0, and finally by index among equal keys.
+// An all-zero chunk (max key 0) keeps indices 0..63 directly.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "sparseloco.h"
+#include "wave.h"
+
+namespace sl {
+namespace {
+
+constexpr int kPerLane = SL_CHUNK / kWave;  // 64 elements per lane
+constexpr int kSlots = kPerLane / 4;        // 16 float4 per lane
+constexpr int kLdsWords = 2048;             // per wavefront
+constexpr uint32_t kKeyMask = 0x7fffffffu;
+constexpr uint32_t kSignBit = 0x80000000u;
+
+static_assert(SL_TOPK == kWave, "one kept entry per lane");
+static_assert(SL_INDEX_BITS == 12 && SL_CODE_BITS == 2, "payload layout");
+
+__device__ __forceinline__ uint32_t key_of(float v) { return __float_as_uint(v) & kKeyMask; }
+
+// In-chunk index of register slot q = 4*m + j of this lane.
+__device__ __forceinline__ uint32_t elem_index(int q, int lane) {
+    return (uint32_t)(256 * (q >> 2) + 4 * lane + (q & 3));
+}
+
+// The kept set is {x : key > key_cut} plus, when tie is set, the entries with
+// key == key_cut and index <= idx_cut; without tie it is {x : key >= key_cut}.
+struct Cut {
+    uint32_t key;
+    uint32_t idx;
+    bool tie;
+};
+
+struct Boundary {
+    uint32_t digit;  // histogram bin holding the cut
+    uint32_t above;  // entries in higher bins
+    uint32_t count;  // entries in the bin itself
+};
+
+__device__ __forceinline__ void clear_words(uint32_t* p, int words, int lane) {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (int w = lane * 4; w < words; w += kWave * 4) *reinterpret_cast<uint4*>(p + w) = z;
+}
+
+// Bin d with count(bins > d) < need <= count(bins >= d).  Lane l owns bins
+// [l*B, l*B + B); each lane reads its bins starting at a lane-dependent
+// rotation so that the 16-byte reads spread over the LDS banks.
+template <int B>
+__device__ __forceinline__ Boundary find_boundary(const uint32_t* hist, uint32_t need, int lane) {
+    static_assert(B % 4 == 0 && ((B / 4) & (B / 4 - 1)) == 0, "bins per lane");
+    uint32_t sum = 0;
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist + lane * B);
+#pragma unroll
+    for (int r = 0; r < B / 4; ++r) {
+        const uint4 v = h4[(r + lane) & (B / 4 - 1)];
+        sum += v.x + v.y + v.z + v.w;
+    }
+    const uint32_t S = wave_suffix_sum(sum, lane);
+    int L = __popcll(ballot(S >= need)) - 1;
+    L = L < 0 ? 0 : L;
+    const uint32_t above_lane = read_lane(S, L) - read_lane(sum, L);
+    const uint32_t h = lane < B ? hist[L * B + lane] : 0u;
+    const uint32_t T = wave_suffix_sum(h, lane);
+    int t = __popcll(ballot(lane < B && T + above_lane >= need)) - 1;
+    t = t < 0 ? 0 : t;
+    Boundary b;
+    b.count = read_lane(h, t);
+    b.digit = (uint32_t)(L * B + t);
+    b.above = above_lane + read_lane(T, t) - b.count;
+    return b;
+}
+
+// Histogram of key bits [SHIFT, SHIFT+10) over entries whose resolved bits
+// match prefix.  A slot where every matching lane falls in the same bin adds
+// its count with one atomic (heavy ties, e.g. many exact zeros).
+template <int SHIFT>
+__device__ __forceinline__ void refine_histogram(const float (&acc)[kPerLane], uint32_t* hist,
+                                 uint32_t pmask, uint32_t prefix, int lane) {
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        const uint32_t k = key_of(acc[q]);
+        const bool c = (k & pmask) == prefix;
+        const uint64_t bm = ballot(c);
+        if (bm) {
+            const uint32_t bin = (k >> SHIFT) & 1023u;
+            const int first = __ffsll((unsigned long long)bm) - 1;
+            const uint32_t b0 = read_lane(bin, first);
+            const uint64_t same = ballot(c && bin == b0);
+            if (same == bm) {
+                if (lane == first) lds_add(&hist[b0], (uint32_t)__popcll(bm));
+            } else if (c) {
+                lds_add(&hist[bin], 1u);
+            }
+        }
+    }
+}
+
+// At most 64 candidates (resolved bits == prefix): rank them exactly by
+// (key descending, index ascending) and return the one at position need-1.
+// Candidates share the resolved bits, so (low key bits, 4095 - index) fits
+// one 32-bit sort word.
+__device__ __forceinline__ Cut rank_cut(const float (&acc)[kPerLane], uint32_t* list, uint32_t pmask,
+                        uint32_t prefix, uint32_t lowmask, uint32_t need, uint32_t cnt,
+                        int lane) {
+    uint32_t base = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        const uint32_t k = key_of(acc[q]);
+        const bool c = (k & pmask) == prefix;
+        const uint64_t bm = ballot(c);
+        if (bm) {
+            const uint32_t pos = base + lanes_below(bm);
+            if (c && pos < (uint32_t)kWave)
+                list[pos] = ((k & lowmask) << 12) | (4095u - elem_index(q, lane));
+            base += (uint32_t)__popcll(bm);
+        }
+    }
+    wave_sync();
+    const bool mine = (uint32_t)lane < cnt;
+    const uint32_t sk = mine ? list[lane] : 0u;
+    uint32_t rank = 0;
+    for (uint32_t f = 0; f < cnt; ++f) rank += read_lane(sk, (int)f) > sk ? 1u : 0u;
+    const uint64_t hit = ballot(mine && rank == need - 1u);
+    const int wl = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    const uint32_t sk_cut = read_lane(sk, wl);
+    const uint64_t same = ballot(mine && (sk >> 12) == (sk_cut >> 12));
+    Cut cut;
+    cut.key = prefix | (sk_cut >> 12);
+    cut.idx = 4095u - (sk_cut & 4095u);
+    cut.tie = __popcll(same) > 1;
+    return cut;
+}
+
+// More than 64 entries share the exact key K: the cut is the need-th smallest
+// index among them, found from a 4096-bit LDS bitmap.
+__device__ __forceinline__ Cut index_cut(const float (&acc)[kPerLane], uint32_t* bm, uint32_t K,
+                         uint32_t need, int lane) {
+    reinterpret_cast<uint2*>(bm)[lane] = make_uint2(0u, 0u);
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        if (key_of(acc[q]) == K) {
+            const uint32_t i = elem_index(q, lane);
+            lds_or(&bm[i >> 5], 1u << (i & 31));
+        }
+    }
+    wave_sync();
+    const uint2 wv = reinterpret_cast<const uint2*>(bm)[lane];  // indices [64l, 64l+64)
+    const uint64_t w = ((uint64_t)wv.y << 32) | wv.x;
+    const uint32_t c = (uint32_t)__popcll(w);
+    const uint32_t incl = wave_prefix_sum(c, lane);
+    const uint64_t reach = ballot(incl >= need);
+    const int L = reach ? __ffsll((unsigned long long)reach) - 1 : 0;
+    const uint32_t r = need - (read_lane(incl, L) - read_lane(c, L));  // 1..64
+    uint64_t wl = ((uint64_t)read_lane(wv.y, L) << 32) | read_lane(wv.x, L);
+    for (uint32_t i = 1; i < r && i < 64u; ++i) wl &= wl - 1;
+    Cut cut;
+    cut.key = K;
+    cut.idx = 64u * (uint32_t)L + (uint32_t)__builtin_ctzll(wl);
+    cut.tie = true;
+    return cut;
+}
+
+__device__ __forceinline__ Cut select_cut(const float (&acc)[kPerLane], uint32_t* lds, uint32_t mx, int lane) {
+    if (mx == 0u) {
+        Cut cut;  // all keys are 0: the lower-index rule keeps 0..63
+        cut.key = 0u;
+        cut.idx = 63u;
+        cut.tie = true;
+        return cut;
+    }
+    // Level 0: key bits 30..20.
+    clear_words(lds, kLdsWords, lane);
+    wave_sync();
+    uint32_t zeros = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        const uint32_t k = key_of(acc[q]);
+        const bool nz = k != 0u;
+        zeros += (uint32_t)(kWave - __popcll(ballot(nz)));
+        if (nz) lds_add(&lds[k >> 20], 1u);
+    }
+    if (lane == 0 && zeros) lds_add(&lds[0], zeros);
+    wave_sync();
+    Boundary b = find_boundary<kLdsWords / kWave>(lds, (uint32_t)SL_TOPK, lane);
+    uint32_t need = (uint32_t)SL_TOPK - b.above;
+    uint32_t prefix = b.digit << 20;
+    uint32_t pmask = 0x7ff00000u;
+    Cut cut;
+    cut.idx = 0u;
+    cut.tie = false;
+    if (b.count == need) {
+        cut.key = prefix;
+        return cut;
+    }
+    wave_sync();
+    if (b.count <= (uint32_t)kWave) return rank_cut(acc, lds, pmask, prefix, 0x000fffffu, need, b.count, lane);
+
+    // Level 1: key bits 19..10 of the boundary bin.
+    clear_words(lds, 1024, lane);
+    wave_sync();
+    refine_histogram<10>(acc, lds, pmask, prefix, lane);
+    wave_sync();
+    b = find_boundary<1024 / kWave>(lds, need, lane);
+    need -= b.above;
+    prefix |= b.digit << 10;
+    pmask = 0x7ffffc00u;
+    if (b.count == need) {
+        cut.key = prefix;
+        return cut;
+    }
+    wave_sync();
+    if (b.count <= (uint32_t)kWave) return rank_cut(acc, lds, pmask, prefix, 0x3ffu, need, b.count, lane);
+
+    // Level 2: key bits 9..0.
+    clear_words(lds, 1024, lane);
+    wave_sync();
+    refine_histogram<0>(acc, lds, pmask, prefix, lane);
+    wave_sync();
+    b = find_boundary<1024 / kWave>(lds, need, lane);
+    need -= b.above;
+    prefix |= b.digit;
+    pmask = kKeyMask;
+    if (b.count == need) {
+        cut.key = prefix;
+        return cut;
+    }
+    wave_sync();
+    if (b.count <= (uint32_t)kWave) return rank_cut(acc, lds, pmask, prefix, 0u, need, b.count, lane);
+    return index_cut(acc, lds, prefix, need, lane);
+}
+
+// Smallest key k with 3 * value(k) > 2s, so that "magnitude bit set" is the
+// integer test key >= k.  Decided in binary64, where 3v and 2s are exact.  The
+// start is within one step of the answer for finite s; the bounds keep a
+// non-finite s (outside the contract) from looping.
+__device__ __forceinline__ uint32_t magnitude_threshold(float s) {
+    const double two_s = 2.0 * (double)s;
+    uint32_t k = __float_as_uint((float)(two_s / 3.0)) & kKeyMask;
+    for (int i = 0; i < 4 && k > 0u && 3.0 * (double)__uint_as_float(k - 1u) > two_s; ++i) --k;
+    for (int i = 0; i < 4 && !(3.0 * (double)__uint_as_float(k) > two_s); ++i) ++k;
+    return k;
+}
+
+// Spread the 16 low bits of x to the even bit positions of a 32-bit word.
+__device__ __forceinline__ uint32_t spread16(uint32_t x) {
+    x = (x | (x << 8)) & 0x00ff00ffu;
+    x = (x | (x << 4)) & 0x0f0f0f0fu;
+    x = (x | (x << 2)) & 0x33333333u;
+    x = (x | (x << 1)) & 0x55555555u;
+    return x;
+}
+
+template <bool TIE>
+__device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane], const Cut& cut,
+                                                   uint32_t kmag, uint32_t sbits, uint32_t s3bits,
+                                                   float* ef_chunk, uint32_t* ent, int lane) {
+    float4* eo = reinterpret_cast<float4*>(ef_chunk);
+    uint32_t nsel = 0;
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = 4 * m + j;
+            const uint32_t bits = __float_as_uint(acc[q]);
+            const uint32_t k = bits & kKeyMask;
+            const uint32_t idx = elem_index(q, lane);
+            const bool sel = TIE ? (k > cut.key || (k == cut.key && idx <= cut.idx))
+                                 : (k >= cut.key);
+            const bool mag = k >= kmag;
+            const uint32_t dbits = (mag ? sbits : s3bits) | (bits & kSignBit);
+            const float r = acc[q] - __uint_as_float(dbits);
+            o[j] = sel ? r : acc[q];
+            const uint64_t bm = ballot(sel);
+            if (bm) {
+                const uint32_t pos = nsel + lanes_below(bm);
+                if (sel && pos < (uint32_t)SL_TOPK)
+                    ent[pos] = idx | ((((bits >> 31) << 1) | (mag ? 1u : 0u)) << 12);
+                nsel += (uint32_t)__popcll(bm);
+            }
+        }
+        eo[m * kWave + lane] = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    return nsel;
+}
+
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(4))) void compress_kernel(const float* delta, float* ef, float beta,
+                                                         uint8_t* payload, float* scales,
+                                                         int64_t n_chunks) {
+    __shared__ __align__(16) uint32_t lds[kLdsWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = (int64_t)blockIdx.x;
+    if (chunk >= n_chunks) return;
+    const size_t base = (size_t)chunk * SL_CHUNK;
+
+    // Error feedback: acc = beta * ef + delta with one rounding.
+    const float4* d4 = reinterpret_cast<const float4*>(delta + base);
+    const float4* e4 = reinterpret_cast<const float4*>(ef + base);
+    float acc[kPerLane];
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        const float4 dv = d4[m * kWave + lane];
+        const float4 ev = e4[m * kWave + lane];
+        acc[4 * m + 0] = __builtin_fmaf(beta, ev.x, dv.x);
+        acc[4 * m + 1] = __builtin_fmaf(beta, ev.y, dv.y);
+        acc[4 * m + 2] = __builtin_fmaf(beta, ev.z, dv.z);
+        acc[4 * m + 3] = __builtin_fmaf(beta, ev.w, dv.w);
+    }
+
+    uint32_t mx = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        const uint32_t k = key_of(acc[q]);
+        mx = k > mx ? k : mx;
+    }
+    mx = uniform(wave_max(mx));
+
+    const Cut cut = select_cut(acc, lds, mx, lane);
+
+    // Scale and levels: s = max |acc| (= the largest kept magnitude).
+    const float s = __uint_as_float(mx);
+    const float s3 = s / 3.0f;
+    const uint32_t kmag = magnitude_threshold(s);
+
+    uint32_t* ent = lds;          // [0, 64)    kept entries, unordered
+    uint32_t* bmp = lds + 64;     // [64, 192)  4096-bit index bitmap
+    uint32_t* pre = lds + 192;    // [192, 256) per-64-index prefix counts
+    uint32_t* sorted = lds + 256; // [256, 320) kept entries in index order
+    wave_sync();
+    if (cut.tie)
+        write_residual<true>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, lane);
+    else
+        write_residual<false>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, lane);
+
+    // Order the 64 entries by index: counting sort through a bitmap.
+    reinterpret_cast<uint2*>(bmp)[lane] = make_uint2(0u, 0u);
+    wave_sync();
+    const uint32_t e = ent[lane];
+    const uint32_t id = e & 4095u;
+    lds_or(&bmp[id >> 5], 1u << (id & 31));
+    wave_sync();
+    const uint2 wv = reinterpret_cast<const uint2*>(bmp)[lane];
+    const uint32_t cnt = (uint32_t)__popcll(((uint64_t)wv.y << 32) | wv.x);
+    pre[lane] = wave_prefix_sum(cnt, lane) - cnt;
+    wave_sync();
+    const uint2 gv = reinterpret_cast<const uint2*>(bmp)[id >> 6];
+    const uint64_t gw = ((uint64_t)gv.y << 32) | gv.x;
+    const uint32_t rank = pre[id >> 6] + (uint32_t)__popcll(gw & ((1ull << (id & 63)) - 1ull));
+    sorted[rank & 63u] = e;
+    wave_sync();
+    const uint32_t es = sorted[lane];
+
+    // Pack: 24 dwords of 12-bit indices, then 4 dwords of 2-bit codes.
+    uint32_t word = 0;
+    if (lane < 24) {
+        const int j0 = (32 * lane) / 12;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int j = j0 + t;
+            const int off = 12 * j - 32 * lane;
+            if (j < SL_TOPK && off < 32) {
+                const uint32_t v = sorted[j] & 4095u;
+                word |= off >= 0 ? (v << off) : (v >> (-off));
+            }
+        }
+    }
+    const uint32_t code = es >> 12;
+    const uint64_t bmag = ballot((code & 1u) != 0u);
+    const uint64_t bsgn = ballot((code & 2u) != 0u);
+    if (lane >= 24 && lane < 28) {
+        const int q = lane - 24;
+        word = spread16((uint32_t)(bmag >> (16 * q)) & 0xffffu) |
+               (spread16((uint32_t)(bsgn >> (16 * q)) & 0xffffu) << 1);
+    }
+    if (lane < SL_PAYLOAD_BYTES / 4)
+        reinterpret_cast<uint32_t*>(payload + (size_t)chunk * SL_PAYLOAD_BYTES)[lane] = word;
+    if (lane == 0) scales[chunk] = s;
+}
+
+}  // namespace
+
+hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* payload,
+                           float* scales, int64_t n_chunks, hipStream_t stream) {
+    void* args[] = {(void*)&delta, (void*)&ef, (void*)&beta, (void*)&payload,
+                    (void*)&scales, (void*)&n_chunks};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel),
+                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
+}
+
+}  // namespace sl

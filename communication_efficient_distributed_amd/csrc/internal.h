@@ -1,0 +1,27 @@
+// internal.h -- launchers shared between the C-ABI layer and the kernel
+// translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sparseloco.h"
+
+namespace sl {
+
+// Pointer table passed by value in the kernel arguments (2 KiB).
+struct PeerTable {
+    const uint8_t* payload[SL_MAX_PEERS];
+    const float* scales[SL_MAX_PEERS];
+};
+
+hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* payload,
+                           float* scales, int64_t n_chunks, hipStream_t stream);
+
+hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
+                            int64_t n_chunks, hipStream_t stream);
+
+hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers,
+                             int64_t n, hipStream_t stream);
+
+}  // namespace sl

@@ -1,0 +1,103 @@
+// sparseloco.cpp -- the C ABI of libsparseloco.so (declared in
+// include/sparseloco.h): host-side argument checks and kernel launches.  No
+// allocation, no state, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "internal.h"
+#include "sparseloco.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+sl_status from_hip(hipError_t e) { return e == hipSuccess ? SL_OK : SL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+sl_status sl_compress(const float* delta, float* ef, float beta, uint8_t* payload,
+                      float* scales, int64_t n, void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n == 0) return SL_OK;
+    if (!delta || !ef || !payload || !scales) return SL_ERR_INVALID_ARG;
+    if (!std::isfinite(beta)) return SL_ERR_INVALID_ARG;
+    if (!aligned(delta, 16) || !aligned(ef, 16) || !aligned(payload, 16) || !aligned(scales, 4))
+        return SL_ERR_ALIGN;
+    const int64_t n_chunks = n / SL_CHUNK;
+    if (n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    const size_t dense = (size_t)n * sizeof(float);
+    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * sizeof(float);
+    if ((const void*)delta != (const void*)ef && overlap(delta, dense, ef, dense))
+        return SL_ERR_INVALID_ARG;
+    if (overlap(payload, pbytes, delta, dense) || overlap(payload, pbytes, ef, dense) ||
+        overlap(scales, sbytes, delta, dense) || overlap(scales, sbytes, ef, dense) ||
+        overlap(payload, pbytes, scales, sbytes))
+        return SL_ERR_INVALID_ARG;
+    return from_hip(sl::launch_compress(delta, ef, beta, payload, scales, n_chunks,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scales,
+                       int32_t n_peers, float* out, int64_t n, void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n == 0) return SL_OK;
+    if (!out) return SL_ERR_INVALID_ARG;
+    if (!aligned(out, 16)) return SL_ERR_ALIGN;
+    const int64_t n_chunks = n / SL_CHUNK;
+    if (n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    const size_t dense = (size_t)n * sizeof(float);
+    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * sizeof(float);
+    sl::PeerTable table = {};
+    if (n_peers > 0 && (!payloads || !scales)) return SL_ERR_INVALID_ARG;
+    for (int32_t p = 0; p < n_peers; ++p) {
+        if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
+        if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
+        if (overlap(out, dense, payloads[p], pbytes) || overlap(out, dense, scales[p], sbytes))
+            return SL_ERR_INVALID_ARG;
+        table.payload[p] = payloads[p];
+        table.scales[p] = scales[p];
+    }
+    return from_hip(sl::launch_aggregate(table, n_peers, out, n_chunks,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
+                        void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n_peers < 1 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n == 0) return SL_OK;
+    if (!theta || !out) return SL_ERR_INVALID_ARG;
+    if (!aligned(theta, 16) || !aligned(out, 16)) return SL_ERR_ALIGN;
+    const size_t dense = (size_t)n * sizeof(float);
+    if (overlap(theta, dense, out, dense)) return SL_ERR_INVALID_ARG;
+    return from_hip(sl::launch_apply_mean(theta, out, n_peers, n,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+const char* sl_status_string(int status) {
+    switch (status) {
+        case SL_OK: return "SL_OK";
+        case SL_ERR_INVALID_ARG: return "SL_ERR_INVALID_ARG: null pointer, non-finite beta or overlapping buffers";
+        case SL_ERR_SHAPE: return "SL_ERR_SHAPE: n must be a non-negative multiple of 4096";
+        case SL_ERR_ALIGN: return "SL_ERR_ALIGN: dense and payload buffers need 16-byte alignment, scales 4-byte";
+        case SL_ERR_TOO_MANY_PEERS: return "SL_ERR_TOO_MANY_PEERS: n_peers outside the allowed range";
+        case SL_ERR_HIP: return "SL_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "unknown sl_status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+/*
+ * sparseloco.h -- C ABI of libsparseloco.so: the SparseLoCo pseudo-gradient
+ * compressor and its aggregator, hand-written HIP for AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *  [SF] "The Sparse Frontier: SparseLoCo and the Compression Math Behind
+ *       Permissionless Pre-Training" (blokz.dev)
+ *  [CV] "Covenant-72B: Decentralized Training is No Longer Just a Dream"
+ *       (wispaper.ai)
+ *
+ * Conventions for every entry point:
+ *  - All buffer pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls and is reentrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns before the GPU finishes; synchronise the stream
+ *    before reading outputs.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    returned as a status; SL_ERR_HIP reports a launch failure.
+ *  - Element counts are int64; n must be a multiple of SL_CHUNK.
+ *  - Inputs must be finite: NaN and Inf are outside the contract (they are
+ *    not detected and give unspecified codes, never out-of-bounds accesses).
+ *  - Results do not depend on the launch configuration: each chunk is owned by
+ *    one wavefront and no floating-point atomics are used, so repeated calls
+ *    are bitwise identical.
+ */
+#ifndef SPARSELOCO_H
+#define SPARSELOCO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* [SF] "Three Compression Levers", lever 1: non-overlapping chunks of 4,096
+ * parameters, the top 64 kept.  Lever 3: 12-bit in-chunk index.  Lever 2: four
+ * 2-bit levels.  Layout formula: 64 x (2 + 12) bits = 112 bytes per chunk. */
+#define SL_CHUNK 4096
+#define SL_TOPK 64
+#define SL_INDEX_BITS 12
+#define SL_CODE_BITS 2
+#define SL_INDEX_BYTES 96     /* 64 x 12 bits */
+#define SL_CODE_BYTES 16      /* 64 x 2 bits */
+#define SL_PAYLOAD_BYTES 112  /* SL_INDEX_BYTES + SL_CODE_BYTES */
+
+/* Peers per sl_aggregate call.  [SF] "Three Compression Levers" reports 24.4
+ * active peers on average out of 70+ unique participants. */
+#define SL_MAX_PEERS 128
+
+#define SL_DEFAULT_BETA 0.95f
+
+typedef enum {
+    SL_OK = 0,
+    SL_ERR_INVALID_ARG = 1,    /* null pointer, non-finite beta, aliasing */
+    SL_ERR_SHAPE = 2,          /* n < 0 or n % SL_CHUNK != 0 */
+    SL_ERR_ALIGN = 3,          /* a buffer is not aligned as documented */
+    SL_ERR_TOO_MANY_PEERS = 4, /* n_peers outside the allowed range */
+    SL_ERR_HIP = 5             /* the HIP runtime reported a launch error */
+} sl_status;
+
+/*
+ * sl_compress -- one SparseLoCo compression round over n parameters.
+ *
+ * Computes, for every chunk c of SL_CHUNK consecutive elements:
+ *   acc[i]   = fma(beta, ef[i], delta[i])       error feedback ([SF] "Why
+ *              Extreme Sparsity Doesn't Break Convergence", error-feedback
+ *              paragraph; beta = 1 is the pages' plain accumulation, the decay
+ *              beta and its single rounding are readings)
+ *   keep the SL_TOPK entries of largest |acc| ([SF] lever 1); ties at the cut
+ *              go to the lower index (reading)
+ *   s        = max |acc| over the chunk (the per-chunk scale of [SF] lever 2;
+ *              reading: the largest kept magnitude)
+ *   code     = (signbit(acc) << 1) | (3|acc| > 2s)   four levels {-s, -s/3,
+ *              +s/3, +s}, s/3 correctly rounded (reading of [SF] lever 2)
+ *   ef[i]    = acc[i] - decoded[i] where kept, acc[i] elsewhere (the
+ *              untransmitted remainder rolls into the next round)
+ *
+ * delta    in   float32[n], 16-byte aligned, read only
+ * ef       in/out float32[n], 16-byte aligned, updated in place; may be the
+ *          same pointer as delta, must not otherwise overlap it
+ * beta     in   finite decay of the error-feedback buffer (default 0.95)
+ * payload  out  uint8[n/4096][112], 16-byte aligned.  Chunk c's record holds
+ *          the 64 kept in-chunk indices in ascending order as 12-bit fields,
+ *          entry j at bits [12j, 12j+12) of bytes 0..95, then the 64 codes as
+ *          2-bit fields, entry j at bits [2j, 2j+2) of bytes 96..111; both are
+ *          little-endian, least-significant-bit-first bit streams
+ * scales   out  float32[n/4096], 4-byte aligned: s of each chunk (not part of
+ *          the 112-byte record; [SF] prices the payload without it)
+ * n        number of parameters, a multiple of SL_CHUNK (0 is a no-op)
+ *
+ * payload and scales must not overlap delta or ef.
+ */
+sl_status sl_compress(const float* delta, float* ef, float beta, uint8_t* payload,
+                      float* scales, int64_t n, void* stream);
+
+/*
+ * sl_aggregate -- decode n_peers payloads and sum them into a dense update.
+ *
+ * [SF] "Why Extreme Sparsity Doesn't Break Convergence", paragraph "Sparse
+ * aggregation can improve model quality": the receivers combine the union of
+ * the peers' selected coordinates.  Reading: the result is the plain sum,
+ * accumulated from +0.0 in ascending peer order for every coordinate, in fp32
+ * with round-to-nearest-even.  out[i] is +0.0 where no peer selected i.
+ *
+ * payloads in  HOST array of n_peers DEVICE pointers, each uint8[n/4096][112]
+ *          in the sl_compress layout, 16-byte aligned
+ * scales   in  HOST array of n_peers DEVICE pointers, each float32[n/4096]
+ * n_peers  0..SL_MAX_PEERS (0 writes all +0.0)
+ * out      out float32[n], 16-byte aligned, fully overwritten; must not overlap
+ *          any payload or scale buffer
+ * n        number of parameters, a multiple of SL_CHUNK
+ *
+ * Payloads are trusted: malformed records (non-increasing indices, negative or
+ * non-finite scales) give unspecified values but every access stays inside the
+ * chunk's own 4096 outputs, since a 12-bit field cannot leave the chunk.  Use
+ * sl_validate_payload for records from untrusted peers.
+ */
+sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scales,
+                       int32_t n_peers, float* out, int64_t n, void* stream);
+
+/*
+ * sl_apply_mean -- outer update with the aggregated sum.
+ *
+ * The pages do not describe the outer optimizer.  Reading: the pseudo-gradient
+ * is pre-loop minus post-loop weights ([SF] "Why DiLoCo Alone Isn't Enough"),
+ * so theta[i] <- theta[i] - out[i] / n_peers with a correctly rounded fp32
+ * division (learning rate 1, no momentum); without compression this is the
+ * mean of the peers' post-loop weights.
+ *
+ * theta    in/out float32[n], 16-byte aligned
+ * out      in  float32[n], 16-byte aligned (the sl_aggregate result)
+ * n_peers  1..SL_MAX_PEERS
+ */
+sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
+                        void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* sl_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSELOCO_H */
