@@ -8,12 +8,20 @@
 // accumulated from +0.0 in ascending peer order for every coordinate.
 //
 // Mapping: one 64-lane wavefront owns one output chunk and a 16 KiB LDS tile of
-// its 4096 sums.  For each peer in order, lane j decodes entry j of that
-// peer's record and adds it into the tile.  Indices within one record are
-// distinct, so the 64 read-modify-writes of a peer never collide, and LDS
-// instructions of one wavefront execute in order, so peer p+1 sees peer p's
-// sums: the result is deterministic and needs no atomics.  The tile is then
-// streamed to HBM with 16-byte stores.
+// its 4096 sums:
+//   1. the peers' 112-byte records are fetched seven lanes x 16 bytes per
+//      peer, nine peers per load instruction, and staged in the tile;
+//   2. lane j reads entry j's 12-bit index and 2-bit code of every peer from
+//      the staged records into registers;
+//   3. the tile is cleared, then peer by peer in order lane j adds entry j.
+//      Indices within one record are distinct, so the 64 read-modify-writes of
+//      a peer never collide, and LDS instructions of one wavefront execute in
+//      order, so peer p+1 sees peer p's sums: deterministic, no atomics;
+//   4. the tile is streamed to HBM with 16-byte stores.
+//
+// Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
+// groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
+// each XCD a contiguous range so a shared line is read through one L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,64 +32,187 @@
 namespace sl {
 namespace {
 
-constexpr int kSlots = SL_CHUNK / (4 * kWave);  // 16 float4 per lane
+constexpr int kSlots = SL_CHUNK / (4 * kWave);     // 16 float4 per lane
+constexpr int kXcds = 8;
+constexpr int kRecWords = SL_PAYLOAD_BYTES / 4;     // 28 dwords per record
+constexpr int kQuads = SL_PAYLOAD_BYTES / 16;       // 7 x 16 bytes per record
+constexpr int kPeersPerLoad = kWave / kQuads;       // 9 records per load instruction
+constexpr int kStagePeers = 3 * kPeersPerLoad;      // 27 records staged at once
 
-__global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32_t n_peers,
-                                                          float* out, int64_t n_chunks) {
-    __shared__ __align__(16) float tile[SL_CHUNK];
-    const int lane = (int)threadIdx.x;
-    const int64_t chunk = (int64_t)blockIdx.x;
-    if (chunk >= n_chunks) return;
+typedef float v4f __attribute__((ext_vector_type(4)));
 
+// Entry j = lane of a staged record: its 12-bit index sits in the 3-byte group
+// of the pair (j & ~1, j | 1) at byte 3*(j >> 1), low half for even j; its
+// 2-bit code is field (j & 15) of code word 24 + (j >> 4).
+struct EntryPos {
+    int w0, sh, cw, csh;
+    __device__ explicit EntryPos(int lane) {
+        const int grp = 3 * (lane >> 1);
+        w0 = grp >> 2;
+        sh = (grp & 3) * 8 + ((lane & 1) ? 12 : 0);
+        cw = SL_INDEX_BYTES / 4 + (lane >> 4);
+        csh = 2 * (lane & 15);
+    }
+    // index | code << 12 of this lane's entry in staged record `rec`
+    __device__ __forceinline__ uint32_t read(const uint32_t* rec) const {
+        const uint32_t a = rec[w0], b = rec[w0 + 1], c = rec[cw];
+        const uint32_t idx = (uint32_t)((((uint64_t)b << 32) | a) >> sh) & 4095u;
+        return idx | (((c >> csh) & 3u) << 12);
+    }
+};
+
+__device__ __forceinline__ void add_entry(float* tile, uint32_t f, float s, float s3) {
+    const uint32_t idx = f & 4095u;
+    const uint32_t code = f >> 12;
+    const float mag = (code & 1u) ? s : s3;
+    const float v = (code & 2u) ? -mag : mag;
+    tile[idx] = tile[idx] + v;
+}
+
+__device__ __forceinline__ void clear_tile(float* tile, int lane) {
     float4* t4 = reinterpret_cast<float4*>(tile);
 #pragma unroll
     for (int m = 0; m < kSlots; ++m) t4[m * kWave + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
-    wave_sync();
+}
 
-    // Entry j = lane: its 12-bit index sits in the 3-byte group of the pair
-    // (j & ~1, j | 1) at byte 3*(j >> 1), low half for even j; its 2-bit code
-    // is field (j & 15) of code word 24 + (j >> 4).
-    const int grp = 3 * (lane >> 1);
-    const int w0 = grp >> 2;
-    const int sh = (grp & 3) * 8 + ((lane & 1) ? 12 : 0);
-    const int cw = SL_INDEX_BYTES / 4 + (lane >> 4);
-    const int csh = 2 * (lane & 15);
-    const size_t rec = (size_t)chunk * SL_PAYLOAD_BYTES;
-
-    for (int p = 0; p < n_peers; ++p) {
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(peers.payload[p] + rec);
-        const uint32_t a = pw[w0];
-        const uint32_t b = pw[w0 + 1];
-        const uint32_t c = pw[cw];
-        const float s = peers.scales[p][chunk];
-        const uint32_t idx = (uint32_t)((((uint64_t)b << 32) | a) >> sh) & 4095u;
-        const uint32_t code = (c >> csh) & 3u;
-        const float s3 = s / 3.0f;
-        const float mag = (code & 1u) ? s : s3;
-        const float v = (code & 2u) ? -mag : mag;
-        tile[idx] = tile[idx] + v;
-    }
-    wave_sync();
-
-    float4* o4 = reinterpret_cast<float4*>(out + (size_t)chunk * SL_CHUNK);
+__device__ __forceinline__ void store_tile(const float* tile, float* out_chunk, int lane) {
+    const float4* t4 = reinterpret_cast<const float4*>(tile);
+    float4* o4 = reinterpret_cast<float4*>(out_chunk);
 #pragma unroll
     for (int m = 0; m < kSlots; ++m) o4[m * kWave + lane] = t4[m * kWave + lane];
 }
 
-// theta <- theta - out / n_peers, 16 bytes per lane per step.
-__global__ __launch_bounds__(256) void apply_mean_kernel(float* theta, const float* out, float nf,
-                                                         int64_t n4) {
-    float4* t4 = reinterpret_cast<float4*>(theta);
-    const float4* o4 = reinterpret_cast<const float4*>(out);
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        float4 t = t4[i];
-        const float4 o = o4[i];
-        t.x = t.x - o.x / nf;
-        t.y = t.y - o.y / nf;
-        t.z = t.z - o.z / nf;
-        t.w = t.w - o.w / nf;
-        t4[i] = t;
+__device__ __forceinline__ int64_t xcd_chunk(int64_t per_xcd) {
+    const int64_t b = (int64_t)blockIdx.x;
+    return (b % kXcds) * per_xcd + b / kXcds;
+}
+
+// Up to 9*NG <= 27 peers (0 allowed), one chunk per workgroup.
+template <int NG>
+__global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32_t n_peers,
+                                                          float* out, int64_t n_chunks,
+                                                          int64_t per_xcd) {
+    constexpr int NP = kPeersPerLoad * NG;
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);  // records staged in the tile
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = xcd_chunk(per_xcd);
+    if (chunk >= n_chunks) return;
+
+    if (n_peers == 0) {  // the empty sum
+        clear_tile(tile, lane);
+        wave_sync();
+        store_tile(tile, out + (size_t)chunk * SL_CHUNK, lane);
+        return;
+    }
+    // Record-load role of this lane: peer 9g + rp, bytes [16 rq, 16 rq + 16).
+    // Every lane loads: lanes without a live peer re-read peer 0's record into
+    // a staging slot nobody reads, which keeps the loads and the staging
+    // registers out of divergent branches.
+    const int rp = lane / kQuads;
+    const int rq = lane - kQuads * rp;
+    const uint8_t* src[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) src[g] = peers.payload[0];
+    const float* ssrc = peers.scales[0];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) {
+        if (p < n_peers) {
+            const uint8_t* pp = peers.payload[p];
+            if (rp == p % kPeersPerLoad) src[p / kPeersPerLoad] = pp;
+            if (lane == p) ssrc = peers.scales[p];
+        }
+    }
+    const size_t off = (size_t)chunk * SL_PAYLOAD_BYTES + 16 * (size_t)rq;
+    const float sv = ssrc[chunk];  // lane p < n_peers: peer p's scale
+    // Slots 0..9*NG hold 9*NG*112 bytes at most, well inside the 16 KiB tile.
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        *reinterpret_cast<uint4*>(stage + (kPeersPerLoad * g + rp) * kRecWords + 4 * rq) =
+            *reinterpret_cast<const uint4*>(src[g] + off);
+    wave_sync();
+    const EntryPos pos(lane);
+    uint32_t f[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        if (p < n_peers) f[p] = pos.read(stage + p * kRecWords);
+    wave_sync();
+    clear_tile(tile, lane);
+    const float s3v = sv / 3.0f;  // lane p: peer p's s/3, correctly rounded
+    wave_sync();
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        if (p < n_peers)
+            add_entry(tile, f[p], __uint_as_float(read_lane(__float_as_uint(sv), p)),
+                      __uint_as_float(read_lane(__float_as_uint(s3v), p)));
+    wave_sync();
+    store_tile(tile, out + (size_t)chunk * SL_CHUNK, lane);
+}
+
+// More than 27 peers: one chunk per workgroup, records staged 27 peers at a
+// time in a separate 3 KiB area so the tile keeps its partial sums.
+__global__ __launch_bounds__(kWave) void aggregate_many_kernel(PeerTable peers, int32_t n_peers,
+                                                               float* out, int64_t n_chunks,
+                                                               int64_t per_xcd) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[kStagePeers * kRecWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = xcd_chunk(per_xcd);
+    if (chunk >= n_chunks) return;
+    const int rp = lane / kQuads;
+    const int rq = lane - kQuads * rp;
+    const EntryPos pos(lane);
+    const size_t off = (size_t)chunk * SL_PAYLOAD_BYTES + 16 * (size_t)rq;
+    clear_tile(tile, lane);
+    for (int p0 = 0; p0 < n_peers; p0 += kStagePeers) {
+        const uint8_t* src[3] = {nullptr, nullptr, nullptr};
+        const float* ssrc = nullptr;
+        for (int q = 0; q < kStagePeers && p0 + q < n_peers; ++q) {
+            const uint8_t* pp = peers.payload[p0 + q];
+            if (rp == q % kPeersPerLoad) src[q / kPeersPerLoad] = pp;
+            if (lane == q) ssrc = peers.scales[p0 + q];
+        }
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+            if (rp < kPeersPerLoad && p0 + kPeersPerLoad * g + rp < n_peers)
+                *reinterpret_cast<uint4*>(stage + (kPeersPerLoad * g + rp) * kRecWords + 4 * rq) =
+                    *reinterpret_cast<const uint4*>(src[g] + off);
+        const float sv = (lane < kStagePeers && p0 + lane < n_peers) ? ssrc[chunk] : 0.0f;
+        const float s3v = sv / 3.0f;
+        wave_sync();
+        for (int q = 0; q < kStagePeers && p0 + q < n_peers; ++q)
+            add_entry(tile, pos.read(stage + q * kRecWords),
+                      __uint_as_float(read_lane(__float_as_uint(sv), q)),
+                      __uint_as_float(read_lane(__float_as_uint(s3v), q)));
+        wave_sync();
+    }
+    store_tile(tile, out + (size_t)chunk * SL_CHUNK, lane);
+}
+
+// theta <- theta - out / n_peers over one 4096-element chunk per wavefront,
+// streaming loads and stores.
+__global__ __launch_bounds__(kWave) void apply_mean_kernel(float* theta, const float* out, float nf,
+                                                           int64_t n_chunks) {
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = (int64_t)blockIdx.x;
+    if (chunk >= n_chunks) return;
+    const size_t base = (size_t)chunk * SL_CHUNK;
+    v4f t[kSlots], o[kSlots];
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+        t[m] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(theta + off));
+        o[m] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(out + off));
+    }
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+        v4f r;
+        r.x = t[m].x - o[m].x / nf;
+        r.y = t[m].y - o[m].y / nf;
+        r.z = t[m].z - o[m].z / nf;
+        r.w = t[m].w - o[m].w / nf;
+        __builtin_nontemporal_store(r, reinterpret_cast<v4f*>(theta + off));
     }
 }
 
@@ -90,22 +221,22 @@ __global__ __launch_bounds__(256) void apply_mean_kernel(float* theta, const flo
 hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
                             int64_t n_chunks, hipStream_t stream) {
     PeerTable t = peers;
-    void* args[] = {(void*)&t, (void*)&n_peers, (void*)&out, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&aggregate_kernel),
-                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
+    const int64_t per_xcd = (n_chunks + kXcds - 1) / kXcds;
+    void* args[] = {(void*)&t, (void*)&n_peers, (void*)&out, (void*)&n_chunks, (void*)&per_xcd};
+    const void* k = n_peers > kStagePeers ? reinterpret_cast<const void*>(&aggregate_many_kernel)
+                    : n_peers > 2 * kPeersPerLoad ? reinterpret_cast<const void*>(&aggregate_kernel<3>)
+                    : n_peers > kPeersPerLoad     ? reinterpret_cast<const void*>(&aggregate_kernel<2>)
+                                                  : reinterpret_cast<const void*>(&aggregate_kernel<1>);
+    return hipLaunchKernel(k, dim3((unsigned)(per_xcd * kXcds)), dim3(kWave), args, 0, stream);
 }
 
 hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
                              hipStream_t stream) {
-    const int64_t n4 = n / 4;
+    int64_t n_chunks = n / SL_CHUNK;
     float nf = (float)n_peers;
-    int64_t blocks = (n4 + 255) / 256;
-    const int64_t cap = 256 * 32;  // 32 workgroups per CU over 256 CUs
-    if (blocks > cap) blocks = cap;
-    if (blocks < 1) blocks = 1;
-    void* args[] = {(void*)&theta, (void*)&out, (void*)&nf, (void*)&n4};
+    void* args[] = {(void*)&theta, (void*)&out, (void*)&nf, (void*)&n_chunks};
     return hipLaunchKernel(reinterpret_cast<const void*>(&apply_mean_kernel),
-                           dim3((unsigned)blocks), dim3(256), args, 0, stream);
+                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
 }
 
 }  // namespace sl

@@ -277,11 +277,24 @@ __device__ __forceinline__ uint32_t spread16(uint32_t x) {
     return x;
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Streaming accesses: delta, ef and the records are touched once per round,
+// so loads and stores carry the nontemporal hint.
+__device__ __forceinline__ float4 stream_load(const float* p) {
+    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void stream_store(float* p, float a, float b, float c, float d) {
+    const v4f v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+}
+
 template <bool TIE>
 __device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane], const Cut& cut,
                                                    uint32_t kmag, uint32_t sbits, uint32_t s3bits,
                                                    float* ef_chunk, uint32_t* ent, int lane) {
-    float4* eo = reinterpret_cast<float4*>(ef_chunk);
     uint32_t nsel = 0;
 #pragma unroll
     for (int m = 0; m < kSlots; ++m) {
@@ -306,34 +319,32 @@ __device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane],
                 nsel += (uint32_t)__popcll(bm);
             }
         }
-        eo[m * kWave + lane] = make_float4(o[0], o[1], o[2], o[3]);
+        stream_store(ef_chunk + 4 * (m * kWave + lane), o[0], o[1], o[2], o[3]);
     }
     return nsel;
 }
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(4))) void compress_kernel(const float* delta, float* ef, float beta,
-                                                         uint8_t* payload, float* scales,
-                                                         int64_t n_chunks) {
-    __shared__ __align__(16) uint32_t lds[kLdsWords];
-    const int lane = (int)threadIdx.x;
-    const int64_t chunk = (int64_t)blockIdx.x;
-    if (chunk >= n_chunks) return;
-    const size_t base = (size_t)chunk * SL_CHUNK;
-
-    // Error feedback: acc = beta * ef + delta with one rounding.
-    const float4* d4 = reinterpret_cast<const float4*>(delta + base);
-    const float4* e4 = reinterpret_cast<const float4*>(ef + base);
-    float acc[kPerLane];
+// acc = beta * ef + delta (one rounding) for the chunk starting at base.
+__device__ __forceinline__ void load_accumulator(const float* delta, const float* ef, float beta,
+                                                 size_t base, int lane, float (&acc)[kPerLane]) {
 #pragma unroll
     for (int m = 0; m < kSlots; ++m) {
-        const float4 dv = d4[m * kWave + lane];
-        const float4 ev = e4[m * kWave + lane];
+        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+        const float4 dv = stream_load(delta + off);
+        const float4 ev = stream_load(ef + off);
         acc[4 * m + 0] = __builtin_fmaf(beta, ev.x, dv.x);
         acc[4 * m + 1] = __builtin_fmaf(beta, ev.y, dv.y);
         acc[4 * m + 2] = __builtin_fmaf(beta, ev.z, dv.z);
         acc[4 * m + 3] = __builtin_fmaf(beta, ev.w, dv.w);
     }
+}
 
+// Everything after the accumulator is formed: selection, scale, residual
+// write-back, ordering and packing of chunk `chunk`.
+__device__ __forceinline__ void compress_chunk(const float (&acc)[kPerLane], uint32_t* lds, float* ef,
+                                               uint8_t* payload, float* scales, int64_t chunk,
+                                               int lane) {
+    const size_t base = (size_t)chunk * SL_CHUNK;
     uint32_t mx = 0;
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
@@ -402,6 +413,18 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(4))) void
     if (lane < SL_PAYLOAD_BYTES / 4)
         reinterpret_cast<uint32_t*>(payload + (size_t)chunk * SL_PAYLOAD_BYTES)[lane] = word;
     if (lane == 0) scales[chunk] = s;
+    wave_sync();   // the LDS slice is reused by the next chunk of this wavefront
+}
+
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void compress_kernel(
+    const float* delta, float* ef, float beta, uint8_t* payload, float* scales, int64_t n_chunks) {
+    __shared__ __align__(16) uint32_t lds[kLdsWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = (int64_t)blockIdx.x;
+    if (chunk >= n_chunks) return;
+    float acc[kPerLane];
+    load_accumulator(delta, ef, beta, (size_t)chunk * SL_CHUNK, lane, acc);
+    compress_chunk(acc, lds, ef, payload, scales, chunk, lane);
 }
 
 }  // namespace

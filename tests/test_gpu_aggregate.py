@@ -35,7 +35,7 @@ def random_peers(orc, n_peers, n_chunks, seed, **kw):
     return payloads, scales
 
 
-@pytest.mark.parametrize("n_peers", [0, 1, 2, 24, 128])
+@pytest.mark.parametrize("n_peers", [0, 1, 2, 9, 10, 18, 19, 24, 27, 28, 55, 128])
 def test_random_records(orc, n_peers):
     sl = require_gpu()
     n_chunks = 64
