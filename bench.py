@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-chunks", type=int, default=8192)
+    ap.add_argument("--cpu-sample-chunks", type=int, default=57344)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a torch copy of 1 GiB (for counter calibration)")
     return ap.parse_args()

@@ -1,0 +1,158 @@
+"""Host-side tests of the C ABI (include/sparseloco.h): the library loads, exports
+every declared entry point, and rejects bad arguments with the documented status
+before anything reaches the GPU.  No compute call is made here.
+
+Pointer arguments are fake addresses: argument checks never dereference them.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparseloco.h")
+
+SL_OK, SL_ERR_INVALID_ARG, SL_ERR_SHAPE, SL_ERR_ALIGN, SL_ERR_TOO_MANY_PEERS, SL_ERR_HIP = range(6)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sl_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from communication_efficient_distributed_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from communication_efficient_distributed_amd import _build
+        _build.build_library()
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("sl_compress", "sl_aggregate", "sl_apply_mean", "sl_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (sl_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_constants_match_pages():
+    """The layout constants in the header: 4096-chunks, top 64, 12-bit indices,
+    2-bit codes, 112-byte records (The Sparse Frontier, Three Compression
+    Levers)."""
+    text = open(HEADER).read()
+    val = lambda k: int(re.search(rf"#define {k} (\d+)", text).group(1))
+    assert val("SL_CHUNK") == 4096 and val("SL_TOPK") == 64
+    assert val("SL_INDEX_BITS") == 12 and val("SL_CODE_BITS") == 2
+    assert val("SL_PAYLOAD_BYTES") == 112 == val("SL_INDEX_BYTES") + val("SL_CODE_BYTES")
+    assert val("SL_TOPK") * (val("SL_INDEX_BITS") + val("SL_CODE_BITS")) == 8 * val("SL_PAYLOAD_BYTES")
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["SL_OK", "SL_ERR_INVALID_ARG", "SL_ERR_SHAPE", "SL_ERR_ALIGN",
+                                 "SL_ERR_TOO_MANY_PEERS", "SL_ERR_HIP"]):
+        assert lib.sl_status_string(code).decode().startswith(name)
+    assert lib.sl_status_string(99).decode() == "unknown sl_status"
+
+
+A = 1 << 20  # fake, 16-byte aligned device addresses far apart
+D, E, P, S, O, T = (A * k for k in (1, 200, 400, 600, 800, 1000))
+N = 16 * 4096
+beta = ctypes.c_float(0.95)
+
+
+def comp(lib, d=D, e=E, b=beta, p=P, s=S, n=N):
+    return lib.sl_compress(d, e, b, p, s, n, None)
+
+
+def test_compress_argument_checks(lib):
+    assert comp(lib, n=4095) == SL_ERR_SHAPE
+    assert comp(lib, n=-4096) == SL_ERR_SHAPE
+    assert comp(lib, n=0) == SL_OK                       # no-op, nothing enqueued
+    assert comp(lib, d=None) == SL_ERR_INVALID_ARG
+    assert comp(lib, e=None) == SL_ERR_INVALID_ARG
+    assert comp(lib, p=None) == SL_ERR_INVALID_ARG
+    assert comp(lib, s=None) == SL_ERR_INVALID_ARG
+    assert comp(lib, b=ctypes.c_float(float("nan"))) == SL_ERR_INVALID_ARG
+    assert comp(lib, b=ctypes.c_float(float("inf"))) == SL_ERR_INVALID_ARG
+    assert comp(lib, d=D + 4) == SL_ERR_ALIGN
+    assert comp(lib, e=E + 8) == SL_ERR_ALIGN
+    assert comp(lib, p=P + 4) == SL_ERR_ALIGN
+    assert comp(lib, s=S + 2) == SL_ERR_ALIGN
+    # overlaps: ef inside delta (but not identical), payload or scales inside delta/ef
+    assert comp(lib, e=D + 4096) == SL_ERR_INVALID_ARG
+    assert comp(lib, p=D + 16) == SL_ERR_INVALID_ARG
+    assert comp(lib, s=E + 64) == SL_ERR_INVALID_ARG
+    assert comp(lib, s=P + 16) == SL_ERR_INVALID_ARG
+
+
+def agg(lib, peers, scales, n_peers, out=O, n=N):
+    pa = (ctypes.c_void_p * max(len(peers), 1))(*peers)
+    sa = (ctypes.c_void_p * max(len(scales), 1))(*scales)
+    return lib.sl_aggregate(ctypes.cast(pa, ctypes.c_void_p), ctypes.cast(sa, ctypes.c_void_p),
+                            n_peers, out, n, None)
+
+
+def test_aggregate_argument_checks(lib):
+    pp = [P + k * A for k in range(3)]
+    ss = [S + k * A for k in range(3)]
+    assert agg(lib, pp, ss, 3, n=100) == SL_ERR_SHAPE
+    assert agg(lib, pp, ss, -1) == SL_ERR_TOO_MANY_PEERS
+    assert agg(lib, pp, ss, 129) == SL_ERR_TOO_MANY_PEERS
+    assert agg(lib, pp, ss, 3, n=0) == SL_OK
+    assert agg(lib, pp, ss, 3, out=None) == SL_ERR_INVALID_ARG
+    assert agg(lib, pp, ss, 3, out=O + 4) == SL_ERR_ALIGN
+    assert agg(lib, [pp[0], None, pp[2]], ss, 3) == SL_ERR_INVALID_ARG
+    assert agg(lib, pp, [ss[0], ss[1], None], 3) == SL_ERR_INVALID_ARG
+    assert agg(lib, [pp[0], pp[1] + 8, pp[2]], ss, 3) == SL_ERR_ALIGN
+    assert agg(lib, pp, [ss[0], ss[1] + 1, ss[2]], 3) == SL_ERR_ALIGN
+    assert agg(lib, [O + 4096] + pp[1:], ss, 3) == SL_ERR_INVALID_ARG      # out overlaps a record
+    assert agg(lib, pp, [O + 64] + ss[1:], 3) == SL_ERR_INVALID_ARG        # out overlaps scales
+    assert lib.sl_aggregate(None, None, 2, O, N, None) == SL_ERR_INVALID_ARG
+
+
+def test_apply_mean_argument_checks(lib):
+    assert lib.sl_apply_mean(T, O, 24, 4097, None) == SL_ERR_SHAPE
+    assert lib.sl_apply_mean(T, O, 0, N, None) == SL_ERR_TOO_MANY_PEERS
+    assert lib.sl_apply_mean(T, O, 129, N, None) == SL_ERR_TOO_MANY_PEERS
+    assert lib.sl_apply_mean(T, O, 24, 0, None) == SL_OK
+    assert lib.sl_apply_mean(None, O, 24, N, None) == SL_ERR_INVALID_ARG
+    assert lib.sl_apply_mean(T, None, 24, N, None) == SL_ERR_INVALID_ARG
+    assert lib.sl_apply_mean(T + 4, O, 24, N, None) == SL_ERR_ALIGN
+    assert lib.sl_apply_mean(T, T + 16, 24, N, None) == SL_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    import communication_efficient_distributed_amd as sl
+    d = torch.zeros(4096)
+    with pytest.raises((ValueError, TypeError)):
+        sl.sl_compress(d, torch.zeros(4096), 0.95, torch.zeros((1, 112), dtype=torch.uint8),
+                       torch.zeros(1))
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """With the library missing, the product path raises; there is no fallback."""
+    code = (
+        "import communication_efficient_distributed_amd._lib as L\n"
+        f"L.LIB_PATH = {str(tmp_path / 'missing.so')!r}\n"
+        "L._handle = None\n"
+        "try:\n"
+        "    L.load()\n"
+        "except L.LibraryMissing as e:\n"
+        "    print('raised', e)\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "raised" in r.stdout, r.stdout + r.stderr
