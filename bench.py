@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the entry points beyond the three-step path")
     ap.add_argument("--cpu-sample-chunks", type=int, default=57344)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a torch copy of 1 GiB (for counter calibration)")
@@ -208,10 +210,53 @@ def main():
         "device": torch.cuda.get_device_name(dev),
     }
 
+    if not args.no_next_rows:
+        result["next_rows"] = next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n,
+                                        stream, kstats)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n)
 
     print(json.dumps(result), flush=True)
+
+
+def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, kstats, reps=5):
+    """The entry points beyond the three-step path, on the same workload (not
+    part of `value`): fused aggregate + outer update, compression straight from
+    pre/post weights, error feedback in pinned host memory, record validation."""
+    import torch
+
+    def timed(fn, k=reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    res = {}
+    t = timed(lambda: sl.sl_aggregate_apply(peer_p, peer_s, theta))
+    res["aggregate_apply_fused"] = kstats(t, 8 + N_PEERS * RECORD / CHUNK)
+    post = torch.empty_like(delta)
+    post.copy_(theta)
+    pre = theta
+    t = timed(lambda: sl.sl_compress_weights(pre, post, ef, BETA, payload, scales))
+    res["compress_weights"] = kstats(t, 16 + RECORD / CHUNK)
+    del post
+    ef_host = torch.zeros(n, dtype=torch.float32, pin_memory=True)
+    t = timed(lambda: sl.sl_compress_host_ef(delta, ef_host, BETA, payload, scales), k=2)
+    st = kstats(t, 4 + RECORD / CHUNK)       # HBM bytes only; ef moves over the host link
+    st["host_link_gb_per_s"] = round(8 * n / (t * 1e-3) / 1e9, 1)
+    res["compress_host_ef"] = st
+    del ef_host
+    flags = torch.empty(n // CHUNK, dtype=torch.uint8, device=delta.device)
+    t = timed(lambda: sl.sl_validate_payload(peer_p[0], peer_s[0], flags))
+    res["validate_one_peer"] = kstats(t, (RECORD + 1) / CHUNK)
+    return res
 
 
 def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):

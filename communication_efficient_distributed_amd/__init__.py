@@ -16,9 +16,14 @@ from ._lib import (  # noqa: F401
     SparseLoCoError,
     aggregate,
     compress,
+    host_device_pointer,
     load,
     sl_aggregate,
+    sl_aggregate_apply,
     sl_apply_mean,
     sl_compress,
+    sl_compress_host_ef,
+    sl_compress_weights,
     sl_status_string,
+    sl_validate_payload,
 )

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsparseloco.so")
 ARCH = "gfx950"
 
-SOURCES = ["sparseloco.cpp", "compress.hip", "aggregate.hip"]
+SOURCES = ["sparseloco.cpp", "compress.hip", "aggregate.hip", "validate.hip"]
 
 DEVICE_FLAGS = [
     "-ffp-contract=off",

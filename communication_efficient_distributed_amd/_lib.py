@@ -28,7 +28,8 @@ STATUS = {
     5: "SL_ERR_HIP",
 }
 
-EXPORTS = ("sl_compress", "sl_aggregate", "sl_apply_mean", "sl_status_string")
+EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_apply",
+           "sl_apply_mean", "sl_validate_payload", "sl_host_device_pointer", "sl_status_string")
 
 
 class SparseLoCoError(RuntimeError):
@@ -57,8 +58,16 @@ def load():
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     L.sl_compress.argtypes = [P, P, F32, P, P, I64, P]
     L.sl_compress.restype = ctypes.c_int
+    L.sl_compress_weights.argtypes = [P, P, P, F32, P, P, I64, P]
+    L.sl_compress_weights.restype = ctypes.c_int
+    L.sl_validate_payload.argtypes = [P, P, I64, P, P]
+    L.sl_validate_payload.restype = ctypes.c_int
+    L.sl_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
+    L.sl_host_device_pointer.restype = ctypes.c_int
     L.sl_aggregate.argtypes = [P, P, I32, P, I64, P]
     L.sl_aggregate.restype = ctypes.c_int
+    L.sl_aggregate_apply.argtypes = [P, P, I32, P, I64, P]
+    L.sl_aggregate_apply.restype = ctypes.c_int
     L.sl_apply_mean.argtypes = [P, P, I32, I64, P]
     L.sl_apply_mean.restype = ctypes.c_int
     L.sl_status_string.argtypes = [ctypes.c_int]
@@ -111,10 +120,66 @@ def sl_compress(delta: torch.Tensor, ef: torch.Tensor, beta: float, payload: tor
         _check("sl_compress", load().sl_compress(*args))
 
 
-def sl_aggregate(payloads, scales, out: torch.Tensor, stream=None) -> None:
-    """out[n] = sum over peers (in list order) of the decoded payloads."""
-    n = out.numel()
+def sl_compress_weights(theta_pre: torch.Tensor, theta_post: torch.Tensor, ef: torch.Tensor,
+                        beta: float, payload: torch.Tensor, scales: torch.Tensor,
+                        stream=None) -> None:
+    """sl_compress with delta = theta_pre - theta_post formed inside the kernel."""
+    n = theta_pre.numel()
+    if theta_post.numel() != n or ef.numel() != n:
+        raise ValueError("theta_pre, theta_post and ef sizes differ")
     C = n // SL_CHUNK
+    if payload.numel() != C * SL_PAYLOAD_BYTES or scales.numel() != C:
+        raise ValueError("payload must hold n/4096*112 bytes and scales n/4096 floats")
+    args = (_dev(theta_pre, "theta_pre", torch.float32), _dev(theta_post, "theta_post", torch.float32),
+            _dev(ef, "ef", torch.float32), ctypes.c_float(beta),
+            _dev(payload, "payload", torch.uint8), _dev(scales, "scales", torch.float32),
+            ctypes.c_int64(n), _stream_of(theta_pre, stream))
+    with torch.cuda.device(theta_pre.device):
+        _check("sl_compress_weights", load().sl_compress_weights(*args))
+
+
+def host_device_pointer(t: torch.Tensor) -> int:
+    """GPU address of a pinned host tensor (raises if it is not pinned and mapped)."""
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError("expected a pinned host tensor (torch.empty(..., pin_memory=True))")
+    out = ctypes.c_void_p()
+    _check("sl_host_device_pointer", load().sl_host_device_pointer(ctypes.c_void_p(t.data_ptr()),
+                                                                   ctypes.byref(out)))
+    return int(out.value)
+
+
+def sl_compress_host_ef(delta: torch.Tensor, ef_host: torch.Tensor, beta: float,
+                        payload: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """sl_compress with the error-feedback buffer offloaded to pinned host memory:
+    the kernel reads and writes it in place over the host link."""
+    n = delta.numel()
+    if ef_host.numel() != n or ef_host.dtype != torch.float32 or not ef_host.is_contiguous():
+        raise ValueError("ef_host must be a contiguous float32 tensor of delta's size")
+    C = n // SL_CHUNK
+    if payload.numel() != C * SL_PAYLOAD_BYTES or scales.numel() != C:
+        raise ValueError("payload must hold n/4096*112 bytes and scales n/4096 floats")
+    ef_dev = host_device_pointer(ef_host)
+    args = (_dev(delta, "delta", torch.float32), ctypes.c_void_p(ef_dev), ctypes.c_float(beta),
+            _dev(payload, "payload", torch.uint8), _dev(scales, "scales", torch.float32),
+            ctypes.c_int64(n), _stream_of(delta, stream))
+    with torch.cuda.device(delta.device):
+        _check("sl_compress", load().sl_compress(*args))
+
+
+def sl_validate_payload(payload: torch.Tensor, scales: torch.Tensor, flags: torch.Tensor,
+                        stream=None) -> None:
+    """flags[c] = 0 for a well-formed record c, else bit 0 = indices not strictly
+    increasing, bit 1 = scale not finite, bit 2 = scale negative."""
+    C = scales.numel()
+    if payload.numel() != C * SL_PAYLOAD_BYTES or flags.numel() != C:
+        raise ValueError("payload must hold C*112 bytes and flags C bytes")
+    args = (_dev(payload, "payload", torch.uint8), _dev(scales, "scales", torch.float32),
+            ctypes.c_int64(C), _dev(flags, "flags", torch.uint8), _stream_of(payload, stream))
+    with torch.cuda.device(payload.device):
+        _check("sl_validate_payload", load().sl_validate_payload(*args))
+
+
+def _peer_arrays(payloads, scales, C):
     if len(payloads) != len(scales):
         raise ValueError("payloads and scales lists differ in length")
     N = len(payloads)
@@ -122,15 +187,31 @@ def sl_aggregate(payloads, scales, out: torch.Tensor, stream=None) -> None:
     sp = (ctypes.c_void_p * max(N, 1))()
     for p in range(N):
         if payloads[p].numel() != C * SL_PAYLOAD_BYTES or scales[p].numel() != C:
-            raise ValueError(f"peer {p}: payload/scales size does not match out")
+            raise ValueError(f"peer {p}: payload/scales size does not match the dense buffer")
         pp[p] = _dev(payloads[p], f"payloads[{p}]", torch.uint8).value
         sp[p] = _dev(scales[p], f"scales[{p}]", torch.float32).value
+    return N, ctypes.cast(pp, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p), (pp, sp)
+
+
+def sl_aggregate(payloads, scales, out: torch.Tensor, stream=None) -> None:
+    """out[n] = sum over peers (in list order) of the decoded payloads."""
+    n = out.numel()
+    N, pa, sa, _keep = _peer_arrays(payloads, scales, n // SL_CHUNK)
     o = _dev(out, "out", torch.float32)
     with torch.cuda.device(out.device):
-        _check("sl_aggregate", load().sl_aggregate(ctypes.cast(pp, ctypes.c_void_p),
-                                                   ctypes.cast(sp, ctypes.c_void_p),
-                                                   ctypes.c_int32(N), o, ctypes.c_int64(n),
+        _check("sl_aggregate", load().sl_aggregate(pa, sa, ctypes.c_int32(N), o, ctypes.c_int64(n),
                                                    _stream_of(out, stream)))
+
+
+def sl_aggregate_apply(payloads, scales, theta: torch.Tensor, stream=None) -> None:
+    """theta <- theta - (sum over peers of the decoded payloads) / n_peers."""
+    n = theta.numel()
+    N, pa, sa, _keep = _peer_arrays(payloads, scales, n // SL_CHUNK)
+    t = _dev(theta, "theta", torch.float32)
+    with torch.cuda.device(theta.device):
+        _check("sl_aggregate_apply", load().sl_aggregate_apply(pa, sa, ctypes.c_int32(N), t,
+                                                               ctypes.c_int64(n),
+                                                               _stream_of(theta, stream)))
 
 
 def sl_apply_mean(theta: torch.Tensor, out: torch.Tensor, n_peers: int, stream=None) -> None:

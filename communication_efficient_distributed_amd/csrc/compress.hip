@@ -339,6 +339,26 @@ __device__ __forceinline__ void load_accumulator(const float* delta, const float
     }
 }
 
+// Pseudo-gradient formed on the fly: delta = theta_pre - theta_post (one fp32
+// subtraction; "Why DiLoCo Alone Isn't Enough" in "The Sparse Frontier" defines
+// the pseudo-gradient as the difference between the pre- and post-inner-loop
+// weights), then acc = beta * ef + delta with one rounding.
+__device__ __forceinline__ void load_accumulator_weights(const float* pre, const float* post,
+                                                         const float* ef, float beta, size_t base,
+                                                         int lane, float (&acc)[kPerLane]) {
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+        const float4 a = stream_load(pre + off);
+        const float4 b = stream_load(post + off);
+        const float4 ev = stream_load(ef + off);
+        acc[4 * m + 0] = __builtin_fmaf(beta, ev.x, a.x - b.x);
+        acc[4 * m + 1] = __builtin_fmaf(beta, ev.y, a.y - b.y);
+        acc[4 * m + 2] = __builtin_fmaf(beta, ev.z, a.z - b.z);
+        acc[4 * m + 3] = __builtin_fmaf(beta, ev.w, a.w - b.w);
+    }
+}
+
 // Everything after the accumulator is formed: selection, scale, residual
 // write-back, ordering and packing of chunk `chunk`.
 __device__ __forceinline__ void compress_chunk(const float (&acc)[kPerLane], uint32_t* lds, float* ef,
@@ -427,7 +447,28 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void
     compress_chunk(acc, lds, ef, payload, scales, chunk, lane);
 }
 
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void compress_weights_kernel(
+    const float* pre, const float* post, float* ef, float beta, uint8_t* payload, float* scales,
+    int64_t n_chunks) {
+    __shared__ __align__(16) uint32_t lds[kLdsWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = (int64_t)blockIdx.x;
+    if (chunk >= n_chunks) return;
+    float acc[kPerLane];
+    load_accumulator_weights(pre, post, ef, beta, (size_t)chunk * SL_CHUNK, lane, acc);
+    compress_chunk(acc, lds, ef, payload, scales, chunk, lane);
+}
+
 }  // namespace
+
+hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
+                                   float beta, uint8_t* payload, float* scales, int64_t n_chunks,
+                                   hipStream_t stream) {
+    void* args[] = {(void*)&theta_pre, (void*)&theta_post, (void*)&ef, (void*)&beta,
+                    (void*)&payload, (void*)&scales, (void*)&n_chunks};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_weights_kernel),
+                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
+}
 
 hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* payload,
                            float* scales, int64_t n_chunks, hipStream_t stream) {

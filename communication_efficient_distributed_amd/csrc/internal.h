@@ -21,6 +21,16 @@ hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* p
 hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
                             int64_t n_chunks, hipStream_t stream);
 
+hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
+                                  int64_t n_chunks, hipStream_t stream);
+
+hipError_t launch_validate(const uint8_t* payload, const float* scales, uint8_t* flags,
+                           int64_t n_chunks, hipStream_t stream);
+
+hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
+                                   float beta, uint8_t* payload, float* scales, int64_t n_chunks,
+                                   hipStream_t stream);
+
 hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers,
                              int64_t n, hipStream_t stream);
 

@@ -49,6 +49,79 @@ sl_status sl_compress(const float* delta, float* ef, float beta, uint8_t* payloa
                                         static_cast<hipStream_t>(stream)));
 }
 
+sl_status sl_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
+                              float beta, uint8_t* payload, float* scales, int64_t n,
+                              void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n == 0) return SL_OK;
+    if (!theta_pre || !theta_post || !ef || !payload || !scales) return SL_ERR_INVALID_ARG;
+    if (!std::isfinite(beta)) return SL_ERR_INVALID_ARG;
+    if (!aligned(theta_pre, 16) || !aligned(theta_post, 16) || !aligned(ef, 16) ||
+        !aligned(payload, 16) || !aligned(scales, 4))
+        return SL_ERR_ALIGN;
+    const int64_t n_chunks = n / SL_CHUNK;
+    if (n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    const size_t dense = (size_t)n * sizeof(float);
+    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * sizeof(float);
+    // theta_pre and theta_post are read only and may alias each other; every
+    // written buffer must be disjoint from every other buffer.
+    const void* in[2] = {theta_pre, theta_post};
+    for (const void* p : in)
+        if (overlap(ef, dense, p, dense) || overlap(payload, pbytes, p, dense) ||
+            overlap(scales, sbytes, p, dense))
+            return SL_ERR_INVALID_ARG;
+    if (overlap(payload, pbytes, ef, dense) || overlap(scales, sbytes, ef, dense) ||
+        overlap(payload, pbytes, scales, sbytes))
+        return SL_ERR_INVALID_ARG;
+    return from_hip(sl::launch_compress_weights(theta_pre, theta_post, ef, beta, payload, scales,
+                                                n_chunks, static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_validate_payload(const uint8_t* payload, const float* scales, int64_t n_chunks,
+                              uint8_t* flags, void* stream) {
+    if (n_chunks < 0 || n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    if (n_chunks == 0) return SL_OK;
+    if (!payload || !scales || !flags) return SL_ERR_INVALID_ARG;
+    if (!aligned(payload, 16) || !aligned(scales, 4)) return SL_ERR_ALIGN;
+    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * sizeof(float);
+    if (overlap(flags, (size_t)n_chunks, payload, pbytes) ||
+        overlap(flags, (size_t)n_chunks, scales, sbytes))
+        return SL_ERR_INVALID_ARG;
+    return from_hip(sl::launch_validate(payload, scales, flags, n_chunks,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validates the peer tables and fills the kernel's pointer table; `dst` (out or
+// theta, float32[n]) must not overlap any record or scale buffer.
+sl_status peer_table(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
+                     const float* dst, int64_t n, sl::PeerTable* table) {
+    const int64_t n_chunks = n / SL_CHUNK;
+    const size_t dense = (size_t)n * sizeof(float);
+    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * sizeof(float);
+    *table = {};
+    if (n_peers > 0 && (!payloads || !scales)) return SL_ERR_INVALID_ARG;
+    for (int32_t p = 0; p < n_peers; ++p) {
+        if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
+        if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
+        if (overlap(dst, dense, payloads[p], pbytes) || overlap(dst, dense, scales[p], sbytes))
+            return SL_ERR_INVALID_ARG;
+        table->payload[p] = payloads[p];
+        table->scales[p] = scales[p];
+    }
+    return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scales,
                        int32_t n_peers, float* out, int64_t n, void* stream) {
     if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
@@ -56,23 +129,27 @@ sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scale
     if (n == 0) return SL_OK;
     if (!out) return SL_ERR_INVALID_ARG;
     if (!aligned(out, 16)) return SL_ERR_ALIGN;
-    const int64_t n_chunks = n / SL_CHUNK;
-    if (n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
-    const size_t dense = (size_t)n * sizeof(float);
-    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
-    const size_t sbytes = (size_t)n_chunks * sizeof(float);
-    sl::PeerTable table = {};
-    if (n_peers > 0 && (!payloads || !scales)) return SL_ERR_INVALID_ARG;
-    for (int32_t p = 0; p < n_peers; ++p) {
-        if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
-        if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
-        if (overlap(out, dense, payloads[p], pbytes) || overlap(out, dense, scales[p], sbytes))
-            return SL_ERR_INVALID_ARG;
-        table.payload[p] = payloads[p];
-        table.scales[p] = scales[p];
-    }
-    return from_hip(sl::launch_aggregate(table, n_peers, out, n_chunks,
+    if (n / SL_CHUNK > 0x7fffffff) return SL_ERR_SHAPE;
+    sl::PeerTable table;
+    const sl_status st = peer_table(payloads, scales, n_peers, out, n, &table);
+    if (st != SL_OK) return st;
+    return from_hip(sl::launch_aggregate(table, n_peers, out, n / SL_CHUNK,
                                          static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_aggregate_apply(const uint8_t* const* payloads, const float* const* scales,
+                             int32_t n_peers, float* theta, int64_t n, void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n_peers < 1 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n == 0) return SL_OK;
+    if (!theta) return SL_ERR_INVALID_ARG;
+    if (!aligned(theta, 16)) return SL_ERR_ALIGN;
+    if (n / SL_CHUNK > 0x7fffffff) return SL_ERR_SHAPE;
+    sl::PeerTable table;
+    const sl_status st = peer_table(payloads, scales, n_peers, theta, n, &table);
+    if (st != SL_OK) return st;
+    return from_hip(sl::launch_aggregate_apply(table, n_peers, theta, n / SL_CHUNK,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
@@ -86,6 +163,18 @@ sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t
     if (overlap(theta, dense, out, dense)) return SL_ERR_INVALID_ARG;
     return from_hip(sl::launch_apply_mean(theta, out, n_peers, n,
                                           static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_host_device_pointer(const void* host_ptr, void** device_ptr) {
+    if (!host_ptr || !device_ptr) return SL_ERR_INVALID_ARG;
+    *device_ptr = nullptr;
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(host_ptr), 0) != hipSuccess || !d) {
+        (void)hipGetLastError();  // clear the error this query may leave behind
+        return SL_ERR_INVALID_ARG;
+    }
+    *device_ptr = d;
+    return SL_OK;
 }
 
 const char* sl_status_string(int status) {

@@ -94,6 +94,24 @@ sl_status sl_compress(const float* delta, float* ef, float beta, uint8_t* payloa
                       float* scales, int64_t n, void* stream);
 
 /*
+ * sl_compress_weights -- sl_compress with the pseudo-gradient formed on the fly.
+ *
+ * The step before compression: "Why DiLoCo Alone Isn't Enough" in [SF] defines
+ * the pseudo-gradient as the difference between the pre- and post-inner-loop
+ * weights.  Reading: delta[i] = theta_pre[i] - theta_post[i] (one fp32
+ * subtraction), then exactly sl_compress(delta, ef, ...), so the results are
+ * bitwise those of materialising delta first; delta never reaches HBM.
+ *
+ * theta_pre, theta_post  in  float32[n], 16-byte aligned, read only (may alias
+ *          each other)
+ * ef, beta, payload, scales, n   as for sl_compress; ef, payload and scales must
+ *          not overlap any other buffer
+ */
+sl_status sl_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
+                              float beta, uint8_t* payload, float* scales, int64_t n,
+                              void* stream);
+
+/*
  * sl_aggregate -- decode n_peers payloads and sum them into a dense update.
  *
  * [SF] "Why Extreme Sparsity Doesn't Break Convergence", paragraph "Sparse
@@ -133,6 +151,59 @@ sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scale
  */
 sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
                         void* stream);
+
+/*
+ * sl_aggregate_apply -- sl_aggregate followed by sl_apply_mean without the dense
+ * update ever reaching HBM.
+ *
+ * The step after aggregation (the outer update; reading as for sl_apply_mean).
+ * For every i: sum = the peer-ordered fp32 sum sl_aggregate would write to
+ * out[i]; theta[i] <- theta[i] - sum / n_peers.  The results are bitwise those
+ * of the two separate calls.  HBM traffic drops from 4 + 12 to 8 bytes per
+ * parameter (plus the records).
+ *
+ * payloads, scales  as for sl_aggregate (host arrays of device pointers)
+ * n_peers  1..SL_MAX_PEERS
+ * theta    in/out float32[n], 16-byte aligned; must not overlap any record or
+ *          scale buffer
+ * n        number of parameters, a multiple of SL_CHUNK
+ */
+sl_status sl_aggregate_apply(const uint8_t* const* payloads, const float* const* scales,
+                             int32_t n_peers, float* theta, int64_t n, void* stream);
+
+/*
+ * sl_validate_payload -- structural checks of received records (untrusted peers).
+ *
+ * [SF] "What the Blockchain Does (and Doesn't Do)": nothing on the chain checks
+ * the updates; the authors' post on the arXiv:2603.08163 listing names integrity
+ * checks among the validator's duties.  Reading of a well-formed record: its 64
+ * indices are strictly increasing and its scale is finite and not negative.
+ *
+ * payload  in  uint8[n_chunks][112], 16-byte aligned
+ * scales   in  float32[n_chunks], 4-byte aligned
+ * n_chunks number of records (0 is a no-op)
+ * flags    out uint8[n_chunks], must not overlap payload or scales; flags[c] is 0
+ *          for a well-formed record, else bit 0 = indices not strictly
+ *          increasing, bit 1 = scale not finite, bit 2 = scale negative
+ */
+sl_status sl_validate_payload(const uint8_t* payload, const float* scales, int64_t n_chunks,
+                              uint8_t* flags, void* stream);
+
+/*
+ * sl_host_device_pointer -- device address of pinned, mapped host memory.
+ *
+ * Error-feedback offload ([CV] "SparseLoCo: Breaking the Bandwidth Barrier":
+ * the error-feedback buffers are moved off the GPU while they are not needed):
+ * an ef buffer in pinned host memory can be passed to sl_compress /
+ * sl_compress_weights through the address returned here; the kernel then reads
+ * and writes it over the host link while delta and the records stay in HBM.
+ *
+ * host_ptr    in  an address inside a pinned host allocation (hipHostMalloc)
+ * device_ptr  out the address the GPU uses for it (NULL on error)
+ * Returns SL_ERR_INVALID_ARG if host_ptr is not pinned and mapped; no kernel
+ * should be given such an address.
+ */
+sl_status sl_host_device_pointer(const void* host_ptr, void** device_ptr);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* sl_status_string(int status);

@@ -43,6 +43,8 @@ def lib():
         L.orc_apply_mean.restype = ctypes.c_int
         L.orc_validate.argtypes = [P, P, i64, P]
         L.orc_validate.restype = ctypes.c_int64
+        L.orc_pseudo_gradient.argtypes = [P, P, i64, P]
+        L.orc_pseudo_gradient.restype = None
         L.orc_decode.argtypes = [ctypes.c_uint8, f32]
         L.orc_decode.restype = f32
         _lib = L
@@ -154,6 +156,15 @@ def validate(payload, scales):
     bad = np.zeros(C, dtype=np.uint8)
     n_bad = lib().orc_validate(_ptr(payload), _ptr(scales), C, _ptr(bad))
     return int(n_bad), bad
+
+
+def pseudo_gradient(theta_pre, theta_post):
+    a = _f32(theta_pre).reshape(-1)
+    b = _f32(theta_post).reshape(-1)
+    assert a.size == b.size
+    d = np.empty_like(a)
+    lib().orc_pseudo_gradient(_ptr(a), _ptr(b), a.size, _ptr(d))
+    return d
 
 
 def decode(code, s):

@@ -50,7 +50,8 @@
  *                          sums, scale doubling, support within the union);
  *                          the peer summation order is reading R9
  *   orc_apply_mean         pinned (closed form on exact inputs)
- *   orc_validate           pinned (hand-made malformed payloads)
+ *   orc_validate           pinned (hand-made malformed payloads, one per flag)
+ *   orc_pseudo_gradient    pinned (exact small-integer weights)
  *   orc_decode             pinned (s/3 against exact-rational rounding)
  */
 #include "oracle.h"
@@ -264,17 +265,29 @@ int orc_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n) {
 
 int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chunks,
                      uint8_t* bad) {
+    /* Reading of a well-formed record: strictly increasing indices, finite and
+     * non-negative scale.  bad[c]: bit 0 order, bit 1 non-finite, bit 2 negative. */
     int64_t n_bad = 0;
     int32_t idx[kTopK];
     uint8_t code[kTopK];
     for (int64_t c = 0; c < n_chunks; ++c) {
         unpack_one(payload + c * kPayloadBytes, idx, code);
-        bool ok = std::isfinite(scales[c]) && scales[c] >= 0.0f;
-        for (int32_t j = 1; j < kTopK; ++j) ok = ok && (idx[j] > idx[j - 1]);
-        if (bad) bad[c] = ok ? 0 : 1;
-        if (!ok) ++n_bad;
+        uint8_t f = 0;
+        for (int32_t j = 1; j < kTopK; ++j)
+            if (!(idx[j] > idx[j - 1])) f |= 1;
+        if (!std::isfinite(scales[c])) f |= 2;
+        if (scales[c] < 0.0f) f |= 4;
+        if (bad) bad[c] = f;
+        if (f) ++n_bad;
     }
     return n_bad;
+}
+
+void orc_pseudo_gradient(const float* theta_pre, const float* theta_post, int64_t n,
+                         float* delta) {
+    /* [SF] "Why DiLoCo Alone Isn't Enough": the pseudo-gradient is the difference
+     * between the pre- and post-inner-loop weights; reading: pre - post. */
+    for (int64_t i = 0; i < n; ++i) delta[i] = theta_pre[i] - theta_post[i];
 }
 
 float orc_decode(uint8_t code, float s) { return decode_value(code, s); }

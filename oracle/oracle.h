@@ -69,10 +69,15 @@ int orc_aggregate(const uint8_t* const* payloads, const float* const* scales,
 int orc_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n);
 
 /* Well-formedness of received payloads: indices strictly increasing, scale
- * finite and >= 0.  bad[c] = 1 for a malformed chunk.  Returns the number of
- * bad chunks. */
+ * finite and >= 0.  bad[c] = 0 for a well-formed chunk, else bit 0 = indices
+ * not strictly increasing, bit 1 = scale not finite, bit 2 = scale negative.
+ * Returns the number of bad chunks. */
 int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chunks,
                      uint8_t* bad);
+
+/* Pseudo-gradient: delta[i] = theta_pre[i] - theta_post[i]. */
+void orc_pseudo_gradient(const float* theta_pre, const float* theta_post, int64_t n,
+                         float* delta);
 
 /* Decoded value of one 2-bit code at chunk scale s. */
 float orc_decode(uint8_t code, float s);

@@ -154,3 +154,26 @@ def test_mlp_8192x28672_full(orc):
     o = orc.aggregate(payloads, scales, n, nthreads=T)
     assert_rel(g, o, "mlp aggregate")
     assert_bitwise(g, o, "mlp aggregate")
+
+
+@pytest.mark.parametrize("n_peers", [1, 9, 10, 24, 28, 128])
+def test_aggregate_apply_fused(orc, n_peers):
+    """sl_aggregate_apply equals the oracle's aggregate followed by apply_mean,
+    and the GPU's own two-call path, bit for bit."""
+    sl = require_gpu()
+    n_chunks = 64
+    n = n_chunks * 4096
+    payloads, scales = random_peers(orc, n_peers, n_chunks, seed=100 + n_peers)
+    theta = datagen.theta0(n, datagen.DECODER_BLOCK).numpy()
+    note(f"sl_aggregate_apply n_peers={n_peers}")
+    pg, sg = to_gpu(payloads), to_gpu(scales)
+    t_fused = torch.from_numpy(theta.copy()).cuda()
+    sl.sl_aggregate_apply(pg, sg, t_fused)
+    t_two = torch.from_numpy(theta.copy()).cuda()
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    sl.sl_aggregate(pg, sg, out)
+    sl.sl_apply_mean(t_two, out, n_peers)
+    torch.cuda.synchronize()
+    want = orc.apply_mean(theta, orc.aggregate(payloads, scales, n), n_peers)
+    assert_bitwise(t_fused.cpu().numpy(), want, "fused vs oracle")
+    assert_bitwise(t_fused.cpu().numpy(), t_two.cpu().numpy(), "fused vs two calls")

@@ -156,4 +156,21 @@ def test_validate_flags_malformed(orc):
     sc2[4] = -1.0
     sc2[5] = np.inf
     n_bad, bad = orc.validate(orc.pack(idx2, code), sc2)
-    assert n_bad == 5 and bad.tolist() == [0, 1, 1, 1, 1, 1]
+    # bit 0: order, bit 1: non-finite scale, bit 2: negative scale
+    assert n_bad == 5 and bad.tolist() == [0, 1, 1, 2, 4, 2]
+    sc3 = sc.copy()
+    sc3[0] = -np.inf
+    sc3[1] = -0.0                                         # -0 is not negative
+    n_bad, bad = orc.validate(orc.pack(idx2, code), sc3)
+    assert bad.tolist()[:3] == [6, 1, 1]
+
+
+def test_pseudo_gradient_exact(orc):
+    """Pre-minus-post weights (The Sparse Frontier, "Why DiLoCo Alone Isn't
+    Enough"): exact on small dyadic weights, sign convention pre - post."""
+    rng = np.random.default_rng(12)
+    pre = (rng.integers(-1000, 1000, 4096) / 64).astype(np.float32)
+    post = (rng.integers(-1000, 1000, 4096) / 64).astype(np.float32)
+    d = orc.pseudo_gradient(pre, post)
+    assert np.array_equal(d.astype(np.float64), pre.astype(np.float64) - post.astype(np.float64))
+    assert orc.pseudo_gradient(np.float32([2.0]), np.float32([0.5]))[0] == 1.5
