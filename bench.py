@@ -241,9 +241,8 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     res = {}
     t = timed(lambda: sl.sl_aggregate_apply(peer_p, peer_s, theta))
     res["aggregate_apply_fused"] = kstats(t, 8 + N_PEERS * RECORD / CHUNK)
-    post = torch.empty_like(delta)
-    post.copy_(theta)
     pre = theta
+    post = theta - delta               # so that pre - post carries the workload's values
     t = timed(lambda: sl.sl_compress_weights(pre, post, ef, BETA, payload, scales))
     res["compress_weights"] = kstats(t, 16 + RECORD / CHUNK)
     del post

@@ -43,6 +43,13 @@ constexpr int kStagePeers = 3 * kPeersPerLoad;      // 27 records staged at once
 #define SL_AGG_CHUNKS_PER_WAVE 4
 #endif
 constexpr int kChunksPerWave = SL_AGG_CHUNKS_PER_WAVE;
+// The fused update also holds theta's chunk in registers; one chunk per
+// wavefront measured fastest for it (341 us against 350 us at two and 360 us
+// at four, 8192 x 28672 parameters, 24 peers).
+#ifndef SL_AGG_APPLY_CHUNKS_PER_WAVE
+#define SL_AGG_APPLY_CHUNKS_PER_WAVE 1
+#endif
+constexpr int kApplyChunksPerWave = SL_AGG_APPLY_CHUNKS_PER_WAVE;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -298,7 +305,7 @@ hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
 
 hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
                                   int64_t n_chunks, hipStream_t stream) {
-    return launch_aggregate_impl<true>(peers, n_peers, theta, n_chunks, stream);
+    return launch_aggregate_impl<true, kApplyChunksPerWave>(peers, n_peers, theta, n_chunks, stream);
 }
 
 hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
