@@ -16,6 +16,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -160,14 +161,18 @@ def main():
     avg = lambda xs: float(sum(xs) / len(xs))
     tc, ta, tm = avg(t_c), avg(t_a), avg(t_m)
 
-    def kstats(t_ms, bpp):
+    def kstats(t_ms, bpp, samples=None):
         gps = n / (t_ms * 1e-3) / 1e9
         gbs = bpp * n / (t_ms * 1e-3) / 1e9
-        return {"ms": round(t_ms, 5), "gparams_per_s": round(gps, 2), "gb_per_s": round(gbs, 1),
-                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_param": round(bpp, 4)}
+        r = {"ms": round(t_ms, 5), "gparams_per_s": round(gps, 2), "gb_per_s": round(gbs, 1),
+             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_param": round(bpp, 4)}
+        if samples:
+            r["ms_median"] = round(statistics.median(samples), 5)
+            r["ms_min"] = round(min(samples), 5)
+        return r
 
     value = n / (ms_per_step * 1e-3) / 1e9
-    comp = kstats(tc, BYTES_COMPRESS)
+    comp = kstats(tc, BYTES_COMPRESS, t_c)
     traffic = traffic_from_profile(n)
     result = {
         "metric": METRIC,
@@ -202,8 +207,8 @@ def main():
         },
         "kernels": {
             "compress": comp,
-            "aggregate": kstats(ta, BYTES_AGGREGATE),
-            "apply_mean": kstats(tm, BYTES_APPLY),
+            "aggregate": kstats(ta, BYTES_AGGREGATE, t_a),
+            "apply_mean": kstats(tm, BYTES_APPLY, t_m),
             "compress_plus_aggregate": kstats(tc + ta, BYTES_COMPRESS + BYTES_AGGREGATE),
         },
         "wall_s_timed": round(wall, 4),
@@ -220,14 +225,15 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, kstats, reps=5):
+def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, kstats, reps=20):
     """The entry points beyond the three-step path, on the same workload (not
     part of `value`): fused aggregate + outer update, compression straight from
     pre/post weights, error feedback in pinned host memory, record validation."""
     import torch
 
-    def timed(fn, k=reps):
-        fn()
+    def timed(fn, k=reps, warm=3):
+        for _ in range(warm):
+            fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -247,7 +253,7 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     res["compress_weights"] = kstats(t, 16 + RECORD / CHUNK)
     del post
     ef_host = torch.zeros(n, dtype=torch.float32, pin_memory=True)
-    t = timed(lambda: sl.sl_compress_host_ef(delta, ef_host, BETA, payload, scales), k=2)
+    t = timed(lambda: sl.sl_compress_host_ef(delta, ef_host, BETA, payload, scales), k=2, warm=1)
     st = kstats(t, 4 + RECORD / CHUNK)       # HBM bytes only; ef moves over the host link
     st["host_link_gb_per_s"] = round(8 * n / (t * 1e-3) / 1e9, 1)
     res["compress_host_ef"] = st
@@ -258,29 +264,49 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     return res
 
 
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
-    """The CPU oracle on the first S chunks of the same workload, all host
-    threads, same three steps.  Reported as a baseline, not a target."""
+    """The CPU oracle on the first S chunks of the same workload, same three
+    steps, on up to 16 host threads (and on one thread for a smaller sample).
+    Reported as a baseline, not a target."""
     import numpy as np
 
     import oracle
 
+    def run(S, T):
+        m = S * CHUNK
+        d = delta[:m].cpu().numpy()
+        e = ef0_host[:m].copy()
+        pp = [p[:S].cpu().numpy() for p in peer_p]
+        ps = [s[:S].cpu().numpy() for s in peer_s]
+        th = theta[:m].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.compress(d, e, beta=BETA, nthreads=T, inplace=True)
+        agg = oracle.aggregate(pp, ps, m, nthreads=T)
+        oracle.apply_mean(th, agg, N_PEERS)
+        return m, time.perf_counter() - t0
+
     S = min(args.cpu_sample_chunks, n // CHUNK)
-    m = S * CHUNK
-    d = delta[:m].cpu().numpy()
-    e = ef0_host[:m].copy()
-    pp = [p[:S].cpu().numpy() for p in peer_p]
-    ps = [s[:S].cpu().numpy() for s in peer_s]
-    th = theta[:m].cpu().numpy()
-    T = max(1, min(64, os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    oracle.compress(d, e, beta=BETA, nthreads=T, inplace=True)
-    agg = oracle.aggregate(pp, ps, m, nthreads=T)
-    oracle.apply_mean(th, agg, N_PEERS)
-    dt = time.perf_counter() - t0
+    T = max(1, min(16, os.cpu_count() or 1))
+    m, dt = run(S, T)
+    S1 = min(4096, S)
+    m1, dt1 = run(S1, 1)
     return {"value": round(m / dt / 1e9, 5), "unit": "Gparams/s", "cores": T, "kind": "oracle",
             "sample": f"first {S} chunks ({m} params) of the same workload: compress + "
-                      f"aggregate {N_PEERS} peers + apply_mean, {dt:.2f} s wall on {T} threads"}
+                      f"aggregate {N_PEERS} peers + apply_mean, {dt:.2f} s wall on {T} threads",
+            "single_thread": {"value": round(m1 / dt1 / 1e9, 5), "unit": "Gparams/s",
+                              "sample": f"first {S1} chunks, {dt1:.2f} s wall on 1 thread"},
+            "host_cpu": host_cpu_model(), "host_cpus_visible": os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -181,3 +181,23 @@ def random_entries(n_chunks: int, seed: int, k: int = 64, chunk: int = CHUNK,
     lo, hi = scale_range
     scales = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n_chunks)).astype(np.float32)
     return idx, code, scales
+
+
+def random_entries_bulk(n_chunks: int, seed: int, k: int = 64, chunk: int = CHUNK,
+                        scale_range=(1e-3, 10.0)):
+    """Like random_entries, vectorised for millions of chunks.  The k gaps
+    before each kept index are 1 + floor of a random composition of the
+    chunk - k spare positions over k + 1 parts, so indices are strictly
+    increasing and start anywhere from 0; an eighth of the chunks are shifted
+    to end exactly at chunk - 1."""
+    rng = np.random.default_rng(seed)
+    w = rng.random((n_chunks, k + 1))
+    w *= (chunk - k) / w.sum(axis=1, keepdims=True)
+    gaps = np.floor(w[:, :k]).astype(np.int32) + 1
+    idx = np.cumsum(gaps, axis=1, dtype=np.int32) - 1
+    right = rng.random(n_chunks) < 0.125           # an eighth end exactly at chunk - 1
+    idx[right] += (chunk - 1 - idx[right, -1])[:, None]
+    code = rng.integers(0, 4, size=(n_chunks, k), dtype=np.uint8)
+    lo, hi = scale_range
+    scales = np.exp(rng.uniform(math.log(lo), math.log(hi), size=n_chunks)).astype(np.float32)
+    return idx, code, scales

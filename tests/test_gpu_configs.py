@@ -1,8 +1,11 @@
-"""GPU parity at the two largest workloads, on sampled chunks.
+"""GPU parity at the two largest workloads.
 
-Every output of the compressor and the aggregator depends only on its own chunk,
-so comparing the GPU's full-size result with the oracle on a sample of chunks
-(plus the boundary chunks) is exact, not statistical.  The oracle follows the
+The decoder block is compared at every chunk for the compressor rounds and for
+aggregate / apply on oracle-packed records, and on sampled chunks for the full
+compress -> aggregate -> apply chain over 24 peers.  Every output of the
+compressor and the aggregator depends only on its own chunk, so comparing the
+GPU's full-size result with the oracle on a sample of chunks (plus the boundary
+chunks) is exact, not statistical.  The oracle follows the
 sampled chunks through every round from the same seeded inputs, and builds its
 own peer records for them; nothing it consumes comes from the HIP path.
 """
@@ -36,38 +39,52 @@ def sample_chunks(n_chunks, extra, k, seed):
     return np.array(sorted(s), dtype=np.int64)
 
 
-def test_decoder_block_two_rounds_aggregate_apply(orc):
-    """One decoder block of a d=8192, 64-Q/8-KV-head transformer (Q, K, V, O,
-    gate, up, down = 855,638,016 params) compressed as one flat buffer: two
-    rounds from ef = 0, 24 peers aggregated, then theta <- theta - sum/24."""
-    sl = require_gpu()
-    W = datagen.DECODER_BLOCK
-    n = datagen.WORKLOAD_PARAMS[W]
-    C = n // CHUNK
-    T = oracle_threads()
-    dev = torch.device("cuda:0")
+def block_chunk_edges(C):
     edges, off = [0, C - 1], 0
     for _, (a, b) in datagen.BLOCK_SHAPES:
         off += a * b
         edges += [off // CHUNK - 1, off // CHUNK]
-    idx = sample_chunks(C, edges, 2048, seed=4)
-    m = idx.size
+    return edges
 
+
+def test_decoder_block_two_rounds_full(orc):
+    """One decoder block of a d=8192, 64-Q/8-KV-head transformer (Q, K, V, O,
+    gate, up, down = 855,638,016 params) compressed as one flat buffer, two
+    rounds from ef = 0: records, scales and ef compared at every chunk."""
+    sl = require_gpu()
+    W = datagen.DECODER_BLOCK
+    n = datagen.WORKLOAD_PARAMS[W]
+    T = oracle_threads()
+    dev = torch.device("cuda:0")
     ef = torch.zeros(n, dtype=torch.float32, device=dev)
-    ef_o = np.zeros(m * CHUNK, np.float32)
+    ef_o = np.zeros(n, np.float32)
     factors = datagen.group_factors(n, W, 0, dev)
     for rnd in range(2):
         d = datagen.lognormal(n, W, 0, rnd, dev, factors=factors)
         note(f"decoder block round {rnd}: sl_compress n={n}")
         payload, scales = sl.compress(d, ef, 0.95)
         torch.cuda.synchronize()
-        op, os_, ef_o = orc.compress(gather(d, idx).reshape(-1), ef_o, beta=0.95, nthreads=T,
-                                     inplace=True)
-        assert_bitwise(gather_rows(payload, idx), op, f"round {rnd} payload")
-        assert_bitwise(gather_rows(scales, idx), os_, f"round {rnd} scales")
-        assert_bitwise(gather(ef, idx).reshape(-1), ef_o, f"round {rnd} ef")
-        del d, payload, scales
+        op, os_, ef_o = orc.compress(d.cpu().numpy(), ef_o, beta=0.95, nthreads=T, inplace=True)
+        del d
+        assert_bitwise(payload.cpu().numpy(), op, f"round {rnd} payload")
+        assert_bitwise(scales.cpu().numpy(), os_, f"round {rnd} scales")
+        assert_bitwise(ef.cpu().numpy(), ef_o, f"round {rnd} ef")
+        del payload, scales
 
+
+def test_decoder_block_peers_aggregate_apply_sampled(orc):
+    """The chain at the decoder block: 24 peers' deltas compressed from ef = 0,
+    their records aggregated, then theta <- theta - sum/24; compared on 2048
+    sampled chunks plus the chunks on each side of every tensor edge.  The
+    oracle builds its own peer records from the same seeded deltas."""
+    sl = require_gpu()
+    W = datagen.DECODER_BLOCK
+    n = datagen.WORKLOAD_PARAMS[W]
+    C = n // CHUNK
+    T = oracle_threads()
+    dev = torch.device("cuda:0")
+    idx = sample_chunks(C, block_chunk_edges(C), 2048, seed=4)
+    m = idx.size
     peer_p, peer_s, orc_p, orc_s = [], [], [], []
     scratch = torch.zeros(n, dtype=torch.float32, device=dev)
     for p in range(1, 25):
@@ -95,6 +112,42 @@ def test_decoder_block_two_rounds_aggregate_apply(orc):
     assert_rel(g, o, "block aggregate")
     assert_bitwise(g, o, "block aggregate")
     assert_bitwise(gather(theta, idx).reshape(-1), orc.apply_mean(theta_s, o, 24), "block apply")
+
+
+def test_decoder_block_aggregate_apply_full(orc):
+    """Aggregate, apply and the fused aggregate-apply at the decoder block's
+    full size, compared at every element: 24 peers of random well-formed
+    records packed by the oracle (an eighth of the chunks end at index 4095)."""
+    sl = require_gpu()
+    W = datagen.DECODER_BLOCK
+    n = datagen.WORKLOAD_PARAMS[W]
+    C = n // CHUNK
+    T = oracle_threads()
+    dev = torch.device("cuda:0")
+    orc_p, orc_s = [], []
+    for p in range(1, 25):
+        idx, code, sc = datagen.random_entries_bulk(C, (W << 32) | (p << 16) | 0xFFFD)
+        orc_p.append(orc.pack(idx, code))
+        orc_s.append(sc)
+        del idx, code
+    peer_p = [torch.from_numpy(x).to(dev) for x in orc_p]
+    peer_s = [torch.from_numpy(x).to(dev) for x in orc_s]
+    note("decoder block full: sl_aggregate 24 peers")
+    out = sl.aggregate(peer_p, peer_s, n)
+    theta = datagen.theta0(n, W, dev)
+    theta_h = theta.cpu().numpy()
+    fused = theta.clone()
+    note("decoder block full: sl_apply_mean")
+    sl.sl_apply_mean(theta, out, 24)
+    note("decoder block full: sl_aggregate_apply 24 peers")
+    sl.sl_aggregate_apply(peer_p, peer_s, fused)
+    torch.cuda.synchronize()
+    o = orc.aggregate(orc_p, orc_s, n, nthreads=T)
+    assert_bitwise(out.cpu().numpy(), o, "block aggregate (full)")
+    del out
+    want = orc.apply_mean(theta_h, o, 24)
+    assert_bitwise(theta.cpu().numpy(), want, "block apply (full)")
+    assert_bitwise(fused.cpu().numpy(), want, "block fused aggregate-apply (full)")
 
 
 def _free_gpu_bytes():

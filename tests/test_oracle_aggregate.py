@@ -174,3 +174,14 @@ def test_pseudo_gradient_exact(orc):
     d = orc.pseudo_gradient(pre, post)
     assert np.array_equal(d.astype(np.float64), pre.astype(np.float64) - post.astype(np.float64))
     assert orc.pseudo_gradient(np.float32([2.0]), np.float32([0.5]))[0] == 1.5
+
+
+def test_bulk_record_generator_is_well_formed(orc):
+    """The vectorised record generator used at full size gives records the
+    validator accepts, reaching both ends of the chunk."""
+    idx, code, sc = datagen.random_entries_bulk(4096, 99)
+    n_bad, _ = orc.validate(orc.pack(idx, code), sc)
+    assert n_bad == 0
+    assert (idx[:, -1] == 4095).any() and (idx[:, 0] == 0).any()
+    back, bc = orc.unpack(orc.pack(idx, code))
+    assert np.array_equal(back, idx) and np.array_equal(bc, code)
