@@ -78,9 +78,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the compressor and aggregator are "
-              "chunk-local; see the sharding notes in DESIGN.md); run with --gpus 1",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the compressor and aggregator are chunk-local, "
+              "and a multi-GPU run would shard chunk ranges and all-gather the records, which "
+              "is not implemented here; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -52,7 +52,7 @@ def load():
         return _handle
     if not os.path.exists(LIB_PATH):
         raise LibraryMissing(
-            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            f"{LIB_PATH} is not built; run `python communication_efficient_distributed_amd/_build.py` "
             "(hipcc --offload-arch=gfx950) first")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float

@@ -39,6 +39,11 @@ constexpr int kLdsWords = 2048;             // per wavefront
 constexpr uint32_t kKeyMask = 0x7fffffffu;
 constexpr uint32_t kSignBit = 0x80000000u;
 
+// Wavefronts per SIMD the register allocation is sized for.
+#ifndef SL_COMPRESS_WAVES_PER_EU
+#define SL_COMPRESS_WAVES_PER_EU 3
+#endif
+
 static_assert(SL_TOPK == kWave, "one kept entry per lane");
 static_assert(SL_INDEX_BITS == 12 && SL_CODE_BITS == 2, "payload layout");
 
@@ -74,11 +79,15 @@ __device__ __forceinline__ void clear_words(uint32_t* p, int words, int lane) {
 template <int B>
 __device__ __forceinline__ Boundary find_boundary(const uint32_t* hist, uint32_t need, int lane) {
     static_assert(B % 4 == 0 && ((B / 4) & (B / 4 - 1)) == 0, "bins per lane");
+    // Each call recomputes its addresses: kept live across the refinement
+    // passes between two calls, they would cost registers.
+    int rl = lane;
+    asm volatile("" : "+v"(rl));
     uint32_t sum = 0;
-    const uint4* h4 = reinterpret_cast<const uint4*>(hist + lane * B);
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist + rl * B);
 #pragma unroll
     for (int r = 0; r < B / 4; ++r) {
-        const uint4 v = h4[(r + lane) & (B / 4 - 1)];
+        const uint4 v = h4[(r + rl) & (B / 4 - 1)];
         sum += v.x + v.y + v.z + v.w;
     }
     const uint32_t S = wave_suffix_sum(sum, lane);
@@ -436,7 +445,7 @@ __device__ __forceinline__ void compress_chunk(const float (&acc)[kPerLane], uin
     wave_sync();   // the LDS slice is reused by the next chunk of this wavefront
 }
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void compress_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SL_COMPRESS_WAVES_PER_EU))) void compress_kernel(
     const float* delta, float* ef, float beta, uint8_t* payload, float* scales, int64_t n_chunks) {
     __shared__ __align__(16) uint32_t lds[kLdsWords];
     const int lane = (int)threadIdx.x;
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void
     compress_chunk(acc, lds, ef, payload, scales, chunk, lane);
 }
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3))) void compress_weights_kernel(
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SL_COMPRESS_WAVES_PER_EU))) void compress_weights_kernel(
     const float* pre, const float* post, float* ef, float beta, uint8_t* payload, float* scales,
     int64_t n_chunks) {
     __shared__ __align__(16) uint32_t lds[kLdsWords];

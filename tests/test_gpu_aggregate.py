@@ -69,6 +69,27 @@ def test_overlapping_and_extreme_indices(orc):
     assert_bitwise(g, o, "aggregate overlapping")
 
 
+def test_scales_over_every_binade(orc):
+    """One peer, 2^16 chunks whose scales are drawn uniformly over the bit
+    patterns of the non-negative finite floats (zero, denormals, every binade up
+    to the largest finite value): each chunk's decoded values are +-s and +-s/3,
+    so this checks the correctly rounded s/3 and the signs across the whole
+    range, bit for bit."""
+    sl = require_gpu()
+    C = 1 << 16
+    idx, code, _ = datagen.random_entries_bulk(C, 4242)
+    rng = np.random.default_rng(4243)
+    bits_ = rng.integers(0, 0x7F800000, C, dtype=np.uint32)
+    bits_[:4] = [0, 1, 0x007FFFFF, 0x7F7FFFFF]         # zero, smallest and largest denormal, max finite
+    scales = bits_.view(np.float32)
+    payload = orc.pack(idx, code)
+    n = C * 4096
+    note("sl_aggregate scales over every binade")
+    g = gpu_aggregate(sl, [payload], [scales], n)
+    o = orc.aggregate([payload], [scales], n, nthreads=oracle_threads())
+    assert_bitwise(g, o, "aggregate over all binades")
+
+
 def test_attn_8192_compress_rounds_and_aggregate(orc):
     """8192 x 8192 attention projection (67.1M params): ef pre-filled by five
     compress rounds (each checked), a sixth round, then 24 peers whose records
