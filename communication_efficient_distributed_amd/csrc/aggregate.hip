@@ -68,15 +68,34 @@ __device__ __forceinline__ void clear_tile(float* tile, int lane) {
     for (int m = 0; m < kSlots; ++m) t4[m * kWave + lane] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// The dense update is written once and not read back by this kernel: stream it
-// out with nontemporal stores (measured 20% faster than plain stores here).
+// Stores of a dense 16 KiB chunk go through a buffer resource spanning exactly
+// that chunk (range-checked by the hardware) so that they can carry explicit
+// cache-policy bits: nontemporal (nt) with device scope (sc1).  The update (or
+// theta) is written once and not read back by this kernel; at 8192 x 28672
+// parameters these stores measured 20% faster than plain stores, and 2-3%
+// (aggregate) and 0.5% (fused update) faster than nontemporal stores without
+// the scope bit.
+constexpr int kStorePolicy = 2 | 16;      // nt | sc1
+constexpr int kRsrcWord3 = 0x00020000;    // raw 32-bit buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(float* chunk_base) {
+    return __builtin_amdgcn_make_buffer_rsrc(chunk_base, (short)0, SL_CHUNK * (int)sizeof(float),
+                                             kRsrcWord3);
+}
+
+template <int POLICY>
+__device__ __forceinline__ void store_slot(__amdgpu_buffer_rsrc_t r, int m, int lane, v4f w) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, w), r, 16 * (m * kWave + lane), 0,
+                                           POLICY);
+}
+
 __device__ __forceinline__ void store_tile(const float* tile, float* out_chunk, int lane) {
     const float4* t4 = reinterpret_cast<const float4*>(tile);
+    const __amdgpu_buffer_rsrc_t r = chunk_rsrc(out_chunk);
 #pragma unroll
     for (int m = 0; m < kSlots; ++m) {
         const float4 v = t4[m * kWave + lane];
-        const v4f w = {v.x, v.y, v.z, v.w};
-        __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(out_chunk + 4 * (m * kWave + lane)));
+        store_slot<kStorePolicy>(r, m, lane, v4f{v.x, v.y, v.z, v.w});
     }
 }
 
@@ -93,6 +112,7 @@ __device__ __forceinline__ void finish_chunk(const float* tile, float* dst_chunk
                                              float nf, int lane) {
     if constexpr (APPLY) {
         const float4* t4 = reinterpret_cast<const float4*>(tile);
+        const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(dst_chunk);
 #pragma unroll
         for (int m = 0; m < kSlots; ++m) {
             const float4 o = t4[m * kWave + lane];
@@ -101,7 +121,7 @@ __device__ __forceinline__ void finish_chunk(const float* tile, float* dst_chunk
             r.y = th[m].y - o.y / nf;
             r.z = th[m].z - o.z / nf;
             r.w = th[m].w - o.w / nf;
-            __builtin_nontemporal_store(r, reinterpret_cast<v4f*>(dst_chunk + 4 * (m * kWave + lane)));
+            store_slot<kStorePolicy>(rs, m, lane, r);
         }
     } else {
         store_tile(tile, dst_chunk, lane);
