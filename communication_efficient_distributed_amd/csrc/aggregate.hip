@@ -9,15 +9,17 @@
 //
 // Mapping: one 64-lane wavefront owns one output chunk and a 16 KiB LDS tile of
 // its 4096 sums:
-//   1. the peers' 112-byte records are fetched seven lanes x 16 bytes per
-//      peer, nine peers per load instruction, and staged in the tile;
-//   2. lane j reads entry j's 12-bit index and 2-bit code of every peer from
-//      the staged records into registers;
-//   3. the tile is cleared, then peer by peer in order lane j adds entry j.
-//      Indices within one record are distinct, so the 64 read-modify-writes of
-//      a peer never collide, and LDS instructions of one wavefront execute in
-//      order, so peer p+1 sees peer p's sums: deterministic, no atomics;
-//   4. the tile is streamed to HBM with 16-byte stores.
+//   1. every peer's 112-byte record is loaded into registers up front, seven
+//      lanes x 16 bytes per record, nine peers per load instruction;
+//   2. the tile is cleared; then, nine peers at a time, the records are staged
+//      in a 1.1 KiB LDS area, lane j reads entry j's 12-bit index and 2-bit code
+//      of each of them into registers, and peer by peer in order lane j adds
+//      entry j to the tile.  Indices within one record are distinct, so the 64
+//      read-modify-writes of a peer never collide, and LDS instructions of one
+//      wavefront execute in order, so peer p+1 sees peer p's sums:
+//      deterministic, no atomics;
+//   3. the tile is streamed to HBM with 16-byte stores (or, fused, theta is
+//      updated in place).
 //
 // Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
@@ -38,21 +40,18 @@ constexpr int kXcds = 8;
 constexpr int kRecWords = SL_PAYLOAD_BYTES / 4;     // 28 dwords per record
 constexpr int kQuads = SL_PAYLOAD_BYTES / 16;       // 7 x 16 bytes per record
 constexpr int kPeersPerLoad = kWave / kQuads;       // 9 records per load instruction
-constexpr int kStagePeers = 3 * kPeersPerLoad;      // 27 records staged at once
-#ifndef SL_AGG_CHUNKS_PER_WAVE
-#define SL_AGG_CHUNKS_PER_WAVE 4
-#endif
-constexpr int kChunksPerWave = SL_AGG_CHUNKS_PER_WAVE;
-// The fused update also holds theta's chunk in registers; one chunk per
-// wavefront measured fastest for it (341 us against 350 us at two and 360 us
-// at four, 8192 x 28672 parameters, 24 peers).
-#ifndef SL_AGG_APPLY_CHUNKS_PER_WAVE
-#define SL_AGG_APPLY_CHUNKS_PER_WAVE 1
-#endif
-constexpr int kApplyChunksPerWave = SL_AGG_APPLY_CHUNKS_PER_WAVE;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a peer's record through a global (address space 1) pointer.  The
+// peer pointers are picked per lane from the table, which leaves them generic;
+// a generic load would also count against the LDS wait counter, so the first
+// LDS wait of the sums would stall on records still in flight.
+__device__ __forceinline__ v4u load_record16(const uint8_t* p) {
+    typedef const __attribute__((address_space(1))) v4u global_v4u;
+    return *(global_v4u*)(p);
+}
 
 __device__ __forceinline__ void add_entry(float* tile, uint32_t f, float s, float s3) {
     const uint32_t idx = f & 4095u;
@@ -137,133 +136,97 @@ __device__ __forceinline__ void load_theta(const float* theta_chunk, v4f (&th)[k
     }
 }
 
-// Up to 9*NG <= 27 peers.  A workgroup (one wavefront) handles CPW
-// consecutive chunks: all their records are loaded up front (the records of
-// neighbouring chunks share lines, and the later chunks' loads are in flight
-// while the first is decoded), then the chunks are summed one after another in
-// the same tile.  dst is the dense update (0 peers allowed) or, with APPLY,
-// theta (n_peers >= 1).
-template <int NG, bool APPLY, int CPW>
-__global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32_t n_peers,
-                                                          float* dst, int64_t n_chunks,
-                                                          int64_t per_xcd, float nf) {
-    constexpr int NP = kPeersPerLoad * NG;
+// Up to 9 * NGMAX peers, one chunk per workgroup (one wavefront).  Every record
+// slice of the chunk is loaded into registers up front (NGMAX loads of 16 bytes
+// per lane, 9 peers each; lanes past the last peer re-read peer 0, so no load
+// sits in a divergent branch).  The tile keeps the partial sums while the peers
+// are staged 9 at a time in a separate 1.1 KiB area: 17.1 KiB of LDS per
+// workgroup leaves room for 9 of them per CU.  dst is the dense update (0 peers
+// allowed) or, with APPLY, theta (n_peers >= 1).
+template <int NGMAX, bool APPLY>
+__global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32_t n_peers, float* dst,
+                                                          int64_t n_chunks, int64_t per_xcd, float nf) {
+    constexpr int kMaxPeers = kPeersPerLoad * NGMAX;
     __shared__ __align__(16) float tile[SL_CHUNK];
-    uint32_t* stage = reinterpret_cast<uint32_t*>(tile);  // records staged in the tile
-    const int lane = (int)threadIdx.x;
-    const int64_t c0 = CPW * xcd_chunk(per_xcd);  // per_xcd counts groups of CPW chunks
-    if (c0 >= n_chunks) return;
-
-    if (!APPLY && n_peers == 0) {  // the empty sum
-        clear_tile(tile, lane);
-        wave_sync();
-#pragma unroll
-        for (int h = 0; h < CPW; ++h)
-            if (c0 + h < n_chunks) store_tile(tile, dst + (size_t)(c0 + h) * SL_CHUNK, lane);
-        return;
-    }
-    // Record-load role of this lane: peer 9g + rp, bytes [16 rq, 16 rq + 16).
-    // Every lane loads: lanes without a live peer re-read peer 0's record into
-    // a staging slot nobody reads, which keeps the loads and the staging
-    // registers out of divergent branches.  Chunks past the end re-read the
-    // last chunk.
-    const int rp = lane / kQuads;
-    const int rq = lane - kQuads * rp;
-    const uint8_t* src[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) src[g] = peers.payload[0];
-    const float* ssrc = peers.scales[0];
-#pragma unroll
-    for (int p = 1; p < NP; ++p) {
-        if (p < n_peers) {
-            const uint8_t* pp = peers.payload[p];
-            if (rp == p % kPeersPerLoad) src[p / kPeersPerLoad] = pp;
-            if (lane == p) ssrc = peers.scales[p];
-        }
-    }
-    v4u r[CPW][NG];  // native vectors: stays in registers (HIP's uint4 would not)
-    float sv[CPW];  // lane p < n_peers: peer p's scale of chunk c0 + h
-#pragma unroll
-    for (int h = 0; h < CPW; ++h) {
-        const int64_t c = c0 + h < n_chunks ? c0 + h : n_chunks - 1;
-        const size_t off = (size_t)c * SL_PAYLOAD_BYTES + 16 * (size_t)rq;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) r[h][g] = *reinterpret_cast<const v4u*>(src[g] + off);
-        sv[h] = ssrc[c];
-    }
-    const EntryPos pos(lane);
-#pragma unroll
-    for (int h = 0; h < CPW; ++h) {
-        if (c0 + h < n_chunks) {
-            float* dst_chunk = dst + (size_t)(c0 + h) * SL_CHUNK;
-            // Slots 0..9*NG hold 9*NG*112 bytes at most, well inside the tile.
-#pragma unroll
-            for (int g = 0; g < NG; ++g)
-                *reinterpret_cast<v4u*>(stage + (kPeersPerLoad * g + rp) * kRecWords + 4 * rq) = r[h][g];
-            v4f th[kSlots];
-            load_theta<APPLY>(dst_chunk, th, lane);  // in flight while the records are decoded
-            wave_sync();
-            uint32_t f[NP];
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-                if (p < n_peers) f[p] = pos.read(stage + p * kRecWords);
-            wave_sync();
-            clear_tile(tile, lane);
-            const float s3v = sv[h] / 3.0f;  // lane p: peer p's s/3, correctly rounded
-            wave_sync();
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-                if (p < n_peers)
-                    add_entry(tile, f[p], __uint_as_float(read_lane(__float_as_uint(sv[h]), p)),
-                              __uint_as_float(read_lane(__float_as_uint(s3v), p)));
-            wave_sync();
-            finish_chunk<APPLY>(tile, dst_chunk, th, nf, lane);
-            wave_sync();  // the next chunk stages into the tile
-        }
-    }
-}
-
-// More than 27 peers: one chunk per workgroup, records staged 27 peers at a
-// time in a separate 3 KiB area so the tile keeps its partial sums.
-template <bool APPLY>
-__global__ __launch_bounds__(kWave) void aggregate_many_kernel(PeerTable peers, int32_t n_peers,
-                                                               float* dst, int64_t n_chunks,
-                                                               int64_t per_xcd, float nf) {
-    __shared__ __align__(16) float tile[SL_CHUNK];
-    __shared__ __align__(16) uint32_t stage[kStagePeers * kRecWords];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
     const int lane = (int)threadIdx.x;
     const int64_t chunk = xcd_chunk(per_xcd);
     if (chunk >= n_chunks) return;
+    float* dst_chunk = dst + (size_t)chunk * SL_CHUNK;
+    if (!APPLY && n_peers == 0) {  // the empty sum; the peer table is empty
+        clear_tile(tile, lane);
+        wave_sync();
+        store_tile(tile, dst_chunk, lane);
+        return;
+    }
     const int rp = lane / kQuads;
     const int rq = lane - kQuads * rp;
     const EntryPos pos(lane);
     const size_t off = (size_t)chunk * SL_PAYLOAD_BYTES + 16 * (size_t)rq;
-    clear_tile(tile, lane);
-    for (int p0 = 0; p0 < n_peers; p0 += kStagePeers) {
-        const uint8_t* src[3] = {nullptr, nullptr, nullptr};
-        const float* ssrc = nullptr;
-        for (int q = 0; q < kStagePeers && p0 + q < n_peers; ++q) {
-            const uint8_t* pp = peers.payload[p0 + q];
-            if (rp == q % kPeersPerLoad) src[q / kPeersPerLoad] = pp;
-            if (lane == q) ssrc = peers.scales[p0 + q];
-        }
+
+    const uint8_t* src[NGMAX];
 #pragma unroll
-        for (int g = 0; g < 3; ++g)
-            if (rp < kPeersPerLoad && p0 + kPeersPerLoad * g + rp < n_peers)
-                *reinterpret_cast<uint4*>(stage + (kPeersPerLoad * g + rp) * kRecWords + 4 * rq) =
-                    *reinterpret_cast<const uint4*>(src[g] + off);
-        const float sv = (lane < kStagePeers && p0 + lane < n_peers) ? ssrc[chunk] : 0.0f;
-        const float s3v = sv / 3.0f;
-        wave_sync();
-        for (int q = 0; q < kStagePeers && p0 + q < n_peers; ++q)
-            add_entry(tile, pos.read(stage + q * kRecWords),
-                      __uint_as_float(read_lane(__float_as_uint(sv), q)),
-                      __uint_as_float(read_lane(__float_as_uint(s3v), q)));
-        wave_sync();
+    for (int g = 0; g < NGMAX; ++g) src[g] = peers.payload[0];
+#pragma unroll
+    for (int p = 1; p < kMaxPeers; ++p) {
+        if (p < n_peers) {
+            const uint8_t* pp = peers.payload[p];
+            if (rp == p % kPeersPerLoad) src[p / kPeersPerLoad] = pp;
+        }
     }
-    float* dst_chunk = dst + (size_t)chunk * SL_CHUNK;
+    v4u r[NGMAX];
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) r[g] = load_record16(src[g] + off);
+    // lane q < 9: scale of peer 9 g + q (peer 0's for lanes past the last peer)
+    float sv[NGMAX];
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) {
+        const float* ssrc = peers.scales[0];
+#pragma unroll
+        for (int q = 0; q < kPeersPerLoad; ++q) {
+            const int p = kPeersPerLoad * g + q;
+            if (p < n_peers) {
+                const float* sp = peers.scales[p];
+                if (lane == q) ssrc = sp;
+            }
+        }
+        sv[g] = ssrc[chunk];
+    }
+    // With 9 or more loads per lane, wait for all of them here, ahead of the
+    // sums: otherwise the compiler sinks the last load into the group that
+    // consumes it, and its latency lands in the middle of the sums.  (With
+    // fewer loads the staggered issue measured faster.)
+    if constexpr (NGMAX >= 9) {
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(r[g]));
+    }
+    // theta is loaded early unless the records already hold most registers.
+    constexpr bool kEarlyTheta = NGMAX <= 9;
     v4f th[kSlots];
-    load_theta<APPLY>(dst_chunk, th, lane);
+    if constexpr (kEarlyTheta) load_theta<APPLY>(dst_chunk, th, lane);
+
+    const int slot = rp < kPeersPerLoad ? rp : kPeersPerLoad;  // lane 63: dummy slot 9
+    clear_tile(tile, lane);
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) {
+        const int p0 = kPeersPerLoad * g;
+        if (p0 < n_peers) {
+            *reinterpret_cast<v4u*>(stage + slot * kRecWords + 4 * rq) = r[g];
+            wave_sync();
+            uint32_t f[kPeersPerLoad];  // slots past the last peer hold stale bytes, never used
+#pragma unroll
+            for (int q = 0; q < kPeersPerLoad; ++q) f[q] = pos.read(stage + q * kRecWords);
+            const float s3v = sv[g] / 3.0f;
+            wave_sync();
+#pragma unroll
+            for (int q = 0; q < kPeersPerLoad; ++q)
+                if (p0 + q < n_peers)
+                    add_entry(tile, f[q], __uint_as_float(read_lane(__float_as_uint(sv[g]), q)),
+                              __uint_as_float(read_lane(__float_as_uint(s3v), q)));
+        }
+    }
+    if constexpr (!kEarlyTheta) load_theta<APPLY>(dst_chunk, th, lane);
+    wave_sync();
     finish_chunk<APPLY>(tile, dst_chunk, th, nf, lane);
 }
 
@@ -294,25 +257,22 @@ __global__ __launch_bounds__(kWave) void apply_mean_kernel(float* theta, const f
     }
 }
 
-template <bool APPLY, int CPW = kChunksPerWave>
+template <bool APPLY>
 hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float* dst,
                                  int64_t n_chunks, hipStream_t stream) {
     PeerTable t = peers;
     float nf = (float)n_peers;
-    if (n_peers > kStagePeers) {
-        const int64_t per_xcd = (n_chunks + kXcds - 1) / kXcds;
-        void* args[] = {(void*)&t, (void*)&n_peers, (void*)&dst, (void*)&n_chunks, (void*)&per_xcd,
-                        (void*)&nf};
-        return hipLaunchKernel(reinterpret_cast<const void*>(&aggregate_many_kernel<APPLY>),
-                               dim3((unsigned)(per_xcd * kXcds)), dim3(kWave), args, 0, stream);
-    }
-    const int64_t groups = (n_chunks + CPW - 1) / CPW;
-    const int64_t per_xcd = (groups + kXcds - 1) / kXcds;
+    int64_t per_xcd = (n_chunks + kXcds - 1) / kXcds;
     void* args[] = {(void*)&t, (void*)&n_peers, (void*)&dst, (void*)&n_chunks, (void*)&per_xcd,
                     (void*)&nf};
-    const void* k = n_peers > 2 * kPeersPerLoad ? reinterpret_cast<const void*>(&aggregate_kernel<3, APPLY, CPW>)
-                    : n_peers > kPeersPerLoad   ? reinterpret_cast<const void*>(&aggregate_kernel<2, APPLY, CPW>)
-                                                : reinterpret_cast<const void*>(&aggregate_kernel<1, APPLY, CPW>);
+    // The smallest variant that holds every peer's record slice.
+    static_assert(kPeersPerLoad * 15 >= SL_MAX_PEERS, "the widest variant covers SL_MAX_PEERS");
+    const void* k = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_kernel<1, APPLY>)
+                    : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_kernel<2, APPLY>)
+                    : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_kernel<3, APPLY>)
+                    : n_peers <= kPeersPerLoad * 6 ? reinterpret_cast<const void*>(&aggregate_kernel<6, APPLY>)
+                    : n_peers <= kPeersPerLoad * 9 ? reinterpret_cast<const void*>(&aggregate_kernel<9, APPLY>)
+                                                   : reinterpret_cast<const void*>(&aggregate_kernel<15, APPLY>);
     return hipLaunchKernel(k, dim3((unsigned)(per_xcd * kXcds)), dim3(kWave), args, 0, stream);
 }
 
@@ -325,7 +285,7 @@ hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
 
 hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
                                   int64_t n_chunks, hipStream_t stream) {
-    return launch_aggregate_impl<true, kApplyChunksPerWave>(peers, n_peers, theta, n_chunks, stream);
+    return launch_aggregate_impl<true>(peers, n_peers, theta, n_chunks, stream);
 }
 
 hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
