@@ -236,9 +236,10 @@ def main():
 
 
 def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, kstats, reps=20):
-    """The entry points beyond the three-step path, on the same workload (not
-    part of `value`): fused aggregate + outer update, compression straight from
-    pre/post weights, error feedback in pinned host memory, record validation."""
+    """The entry points beyond the compress + aggregate step, on the same
+    workload (not part of `value`): fused aggregate + outer update, compression
+    straight from pre/post weights, error feedback in pinned host memory, record
+    validation for one peer and for all 24 in one launch."""
     import torch
 
     def timed(fn, k=reps, warm=3):
@@ -271,6 +272,9 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     flags = torch.empty(n // CHUNK, dtype=torch.uint8, device=delta.device)
     t = timed(lambda: sl.sl_validate_payload(peer_p[0], peer_s[0], flags))
     res["validate_one_peer"] = kstats(t, (RECORD + 1) / CHUNK)
+    flags_all = torch.empty((N_PEERS, n // CHUNK), dtype=torch.uint8, device=delta.device)
+    t = timed(lambda: sl.sl_validate_payloads(peer_p, peer_s, flags_all))
+    res["validate_24_peers"] = kstats(t, N_PEERS * (RECORD + 1) / CHUNK)
     return res
 
 

@@ -26,4 +26,5 @@ from ._lib import (  # noqa: F401
     sl_compress_weights,
     sl_status_string,
     sl_validate_payload,
+    sl_validate_payloads,
 )

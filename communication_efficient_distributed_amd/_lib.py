@@ -29,7 +29,8 @@ STATUS = {
 }
 
 EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_apply",
-           "sl_apply_mean", "sl_validate_payload", "sl_host_device_pointer", "sl_status_string")
+           "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_host_device_pointer",
+           "sl_status_string")
 
 
 class SparseLoCoError(RuntimeError):
@@ -62,6 +63,8 @@ def load():
     L.sl_compress_weights.restype = ctypes.c_int
     L.sl_validate_payload.argtypes = [P, P, I64, P, P]
     L.sl_validate_payload.restype = ctypes.c_int
+    L.sl_validate_payloads.argtypes = [P, P, I32, I64, P, P]
+    L.sl_validate_payloads.restype = ctypes.c_int
     L.sl_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
     L.sl_host_device_pointer.restype = ctypes.c_int
     L.sl_aggregate.argtypes = [P, P, I32, P, I64, P]
@@ -177,6 +180,21 @@ def sl_validate_payload(payload: torch.Tensor, scales: torch.Tensor, flags: torc
             ctypes.c_int64(C), _dev(flags, "flags", torch.uint8), _stream_of(payload, stream))
     with torch.cuda.device(payload.device):
         _check("sl_validate_payload", load().sl_validate_payload(*args))
+
+
+def sl_validate_payloads(payloads, scales, flags: torch.Tensor, stream=None) -> None:
+    """sl_validate_payload for every peer in one launch: flags is uint8
+    [n_peers, n_chunks], row p for peer p."""
+    N = len(payloads)
+    if flags.dim() != 2 or flags.shape[0] != N:
+        raise ValueError("flags must be a [n_peers, n_chunks] tensor")
+    C = flags.shape[1]
+    N, pa, sa, _keep = _peer_arrays(payloads, scales, C)
+    f = _dev(flags, "flags", torch.uint8)
+    with torch.cuda.device(flags.device):
+        _check("sl_validate_payloads", load().sl_validate_payloads(pa, sa, ctypes.c_int32(N),
+                                                                   ctypes.c_int64(C), f,
+                                                                   _stream_of(flags, stream)))
 
 
 def _peer_arrays(payloads, scales, C):

@@ -24,8 +24,9 @@ hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
 hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
                                   int64_t n_chunks, hipStream_t stream);
 
-hipError_t launch_validate(const uint8_t* payload, const float* scales, uint8_t* flags,
-                           int64_t n_chunks, hipStream_t stream);
+// flags[p * n_chunks + c] for peer p < n_peers and record c < n_chunks.
+hipError_t launch_validate(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
+                           hipStream_t stream);
 
 hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
                                    float beta, uint8_t* payload, float* scales, int64_t n_chunks,

@@ -89,8 +89,31 @@ sl_status sl_validate_payload(const uint8_t* payload, const float* scales, int64
     if (overlap(flags, (size_t)n_chunks, payload, pbytes) ||
         overlap(flags, (size_t)n_chunks, scales, sbytes))
         return SL_ERR_INVALID_ARG;
-    return from_hip(sl::launch_validate(payload, scales, flags, n_chunks,
-                                        static_cast<hipStream_t>(stream)));
+    sl::PeerTable table = {};
+    table.payload[0] = payload;
+    table.scales[0] = scales;
+    return from_hip(sl::launch_validate(table, 1, n_chunks, flags, static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* const* scales,
+                               int32_t n_peers, int64_t n_chunks, uint8_t* flags, void* stream) {
+    if (n_chunks < 0 || n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n_chunks == 0 || n_peers == 0) return SL_OK;
+    if (!payloads || !scales || !flags) return SL_ERR_INVALID_ARG;
+    const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * sizeof(float);
+    const size_t fbytes = (size_t)n_peers * (size_t)n_chunks;
+    sl::PeerTable table = {};
+    for (int32_t p = 0; p < n_peers; ++p) {
+        if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
+        if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
+        if (overlap(flags, fbytes, payloads[p], pbytes) || overlap(flags, fbytes, scales[p], sbytes))
+            return SL_ERR_INVALID_ARG;
+        table.payload[p] = payloads[p];
+        table.scales[p] = scales[p];
+    }
+    return from_hip(sl::launch_validate(table, n_peers, n_chunks, flags, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -190,6 +190,24 @@ sl_status sl_validate_payload(const uint8_t* payload, const float* scales, int64
                               uint8_t* flags, void* stream);
 
 /*
+ * sl_validate_payloads -- sl_validate_payload for n_peers peers in one launch,
+ * so that a round's records are checked before they are aggregated.  Same
+ * reading and checks as sl_validate_payload.
+ *
+ * payloads in  HOST array of n_peers DEVICE pointers, each uint8[n_chunks][112],
+ *          16-byte aligned
+ * scales   in  HOST array of n_peers DEVICE pointers, each float32[n_chunks],
+ *          4-byte aligned
+ * n_peers  0..SL_MAX_PEERS (0 is a no-op), else SL_ERR_TOO_MANY_PEERS
+ * n_chunks records per peer (0 is a no-op)
+ * flags    out uint8[n_peers][n_chunks] (peer-major), must not overlap any
+ *          payload or scale buffer; flags[p * n_chunks + c] as for
+ *          sl_validate_payload
+ */
+sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* const* scales,
+                               int32_t n_peers, int64_t n_chunks, uint8_t* flags, void* stream);
+
+/*
  * sl_host_device_pointer -- device address of pinned, mapped host memory.
  *
  * Error-feedback offload ([CV] "SparseLoCo: Breaking the Bandwidth Barrier":

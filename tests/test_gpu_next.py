@@ -74,6 +74,54 @@ def test_validate_payload_flags(orc):
     assert_bitwise(flags.cpu().numpy(), want, "flags")
 
 
+def test_validate_many_peers_in_one_launch(orc):
+    """sl_validate_payloads over 24 peers and a ragged 1000 records each, with
+    defects planted in some peers (order, duplicates, NaN of either sign, -inf,
+    negative and negative-denormal scales, -0 which is allowed), row by row
+    against the oracle."""
+    sl = require_gpu()
+    N, C = 24, 1000
+    rng = np.random.default_rng(17)
+    payloads, scales, want = [], [], []
+    for p in range(N):
+        idx, code, sc = datagen.random_entries_bulk(C, 900 + p)
+        if p % 3 == 1:
+            rows = rng.choice(C, 40, replace=False)
+            for k, c in enumerate(rows):
+                kind = k % 8
+                if kind == 0:
+                    j = rng.integers(1, 64)
+                    idx[c, [j - 1, j]] = idx[c, [j, j - 1]]
+                elif kind == 1:
+                    j = rng.integers(1, 64)
+                    idx[c, j] = idx[c, j - 1]
+                elif kind == 2:
+                    sc[c] = np.nan
+                elif kind == 3:
+                    sc[c] = np.uint32(0xFFC00001).view(np.float32)    # NaN with the sign bit
+                elif kind == 4:
+                    sc[c] = -np.inf
+                elif kind == 5:
+                    sc[c] = np.uint32(0x80000001).view(np.float32)    # -smallest denormal
+                elif kind == 6:
+                    sc[c] = -0.0                                      # allowed
+                else:
+                    idx[c] = idx[c][::-1]
+        pl = orc.pack(idx, code)
+        payloads.append(pl)
+        scales.append(sc)
+        want.append(orc.validate(pl, sc)[1])
+    assert sum(int((w != 0).sum()) for w in want) == 8 * 35
+    flags = torch.full((N, C), 255, dtype=torch.uint8, device="cuda")
+    note("sl_validate_payloads 24 peers x 1000 records")
+    sl.sl_validate_payloads([torch.from_numpy(x).cuda() for x in payloads],
+                            [torch.from_numpy(x).cuda() for x in scales], flags)
+    torch.cuda.synchronize()
+    got = flags.cpu().numpy()
+    for p in range(N):
+        assert_bitwise(got[p], want[p], f"flags of peer {p}")
+
+
 def test_compressor_output_is_well_formed():
     """Every record the compressor writes passes validation (full MLP shape,
     including its all-zero chunks)."""
