@@ -35,7 +35,9 @@ def random_peers(orc, n_peers, n_chunks, seed, **kw):
     return payloads, scales
 
 
-@pytest.mark.parametrize("n_peers", [0, 1, 2, 9, 10, 18, 19, 24, 27, 28, 55, 128])
+# Peer counts at both ends of every kernel variant (up to 9, 18, 27, 54, 81 and
+# 135 peers' records held per lane).
+@pytest.mark.parametrize("n_peers", [0, 1, 2, 9, 10, 18, 19, 24, 27, 28, 54, 55, 81, 82, 128])
 def test_random_records(orc, n_peers):
     sl = require_gpu()
     n_chunks = 64
@@ -177,7 +179,7 @@ def test_mlp_8192x28672_full(orc):
     assert_bitwise(g, o, "mlp aggregate")
 
 
-@pytest.mark.parametrize("n_peers", [1, 9, 10, 24, 28, 128])
+@pytest.mark.parametrize("n_peers", [1, 9, 10, 24, 28, 64, 81, 128])
 def test_aggregate_apply_fused(orc, n_peers):
     """sl_aggregate_apply equals the oracle's aggregate followed by apply_mean,
     and the GPU's own two-call path, bit for bit."""
@@ -198,3 +200,21 @@ def test_aggregate_apply_fused(orc, n_peers):
     want = orc.apply_mean(theta, orc.aggregate(payloads, scales, n), n_peers)
     assert_bitwise(t_fused.cpu().numpy(), want, "fused vs oracle")
     assert_bitwise(t_fused.cpu().numpy(), t_two.cpu().numpy(), "fused vs two calls")
+
+
+@pytest.mark.parametrize("n_peers,n_chunks", [(24, 1), (24, 13), (1, 7), (128, 3), (60, 9)])
+def test_ragged_chunk_counts(orc, n_peers, n_chunks):
+    """Chunk counts that do not fill the last group of the XCD-contiguous
+    numbering (the grid is rounded up to 8 groups): aggregate and fused update."""
+    sl = require_gpu()
+    n = n_chunks * 4096
+    payloads, scales = random_peers(orc, n_peers, n_chunks, seed=7000 + 10 * n_peers + n_chunks)
+    note(f"ragged: n_peers={n_peers} n_chunks={n_chunks}")
+    g = gpu_aggregate(sl, payloads, scales, n)
+    o = orc.aggregate(payloads, scales, n)
+    assert_bitwise(g, o, "aggregate")
+    theta = datagen.theta0(n, datagen.SMALL_1M).numpy()
+    t = torch.from_numpy(theta.copy()).cuda()
+    sl.sl_aggregate_apply(to_gpu(payloads), to_gpu(scales), t)
+    torch.cuda.synchronize()
+    assert_bitwise(t.cpu().numpy(), orc.apply_mean(theta, o, n_peers), "fused")
