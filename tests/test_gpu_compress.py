@@ -159,3 +159,69 @@ def test_determinism_and_delta_aliasing(orc):
     op, os_, oe = orc.compress(d, d, beta=0.95)
     assert_bitwise(payload.cpu().numpy(), op, "aliased payload")
     assert_bitwise(t.cpu().numpy(), oe, "aliased ef")
+
+
+def test_non_finite_chunks_stay_in_bounds(orc):
+    """NaN and Inf inputs are outside the contract (their codes are
+    unspecified), but they must not make the kernel write outside its chunk or
+    loop without end.  Chunks holding NaN, +-Inf or a NaN error-feedback entry
+    sit between finite chunks in one call.  The finite chunks must still match
+    the oracle bit for bit, and guard regions around every output must be
+    untouched, aggregated too."""
+    sl = require_gpu()
+    C = 12
+    n = C * 4096
+    G = 4096                                              # guard elements on each side
+    rng = np.random.default_rng(99)
+    d = (rng.standard_normal(n) * 0.3).astype(np.float32)
+    e = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    bad = {2: "nan", 5: "inf", 6: "mixed", 9: "ef_nan"}
+    for c, kind in bad.items():
+        s = slice(c * 4096, (c + 1) * 4096)
+        if kind == "nan":
+            d[s][::7] = np.nan
+        elif kind == "inf":
+            d[s][::11] = np.inf
+            d[s][5] = -np.inf
+        elif kind == "mixed":
+            d[s][:100] = np.nan
+            d[s][100:164] = np.inf
+        else:
+            e[s][17] = np.nan
+    dev = torch.device("cuda:0")
+    sentinel = np.float32(-12345.5)
+    dbuf = torch.full((n + 2 * G,), float(sentinel), dtype=torch.float32, device=dev)
+    ebuf = torch.full((n + 2 * G,), float(sentinel), dtype=torch.float32, device=dev)
+    pbuf = torch.full(((C + 2) * 112,), 0xA5, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((C + 2 * 16,), float(sentinel), dtype=torch.float32, device=dev)
+    dbuf[G:G + n] = torch.from_numpy(d).to(dev)
+    ebuf[G:G + n] = torch.from_numpy(e).to(dev)
+    payload = pbuf[112:112 + C * 112].view(C, 112)
+    scales = sbuf[16:16 + C]
+    note("non-finite chunks: sl_compress")
+    sl.sl_compress(dbuf[G:G + n], ebuf[G:G + n], 0.95, payload, scales)
+    torch.cuda.synchronize()
+    eb, pb, sb = ebuf.cpu().numpy(), pbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert (eb[:G].view(np.uint32) == sentinel.view(np.uint32)).all()
+    assert (eb[G + n:].view(np.uint32) == sentinel.view(np.uint32)).all()
+    assert (pb[:112] == 0xA5).all() and (pb[112 + C * 112:] == 0xA5).all()
+    assert (sb[:16].view(np.uint32) == sentinel.view(np.uint32)).all()
+    assert (sb[16 + C:].view(np.uint32) == sentinel.view(np.uint32)).all()
+    good = [c for c in range(C) if c not in bad]
+    gd = np.concatenate([d[c * 4096:(c + 1) * 4096] for c in good])
+    ge = np.concatenate([e[c * 4096:(c + 1) * 4096] for c in good])
+    op, os_, oe = orc.compress(gd, ge, beta=0.95)
+    gp = payload.cpu().numpy()[good]
+    assert_bitwise(gp, op, "finite chunks' payload")
+    assert_bitwise(scales.cpu().numpy()[good], os_, "finite chunks' scales")
+    ef_new = eb[G:G + n]
+    assert_bitwise(np.concatenate([ef_new[c * 4096:(c + 1) * 4096] for c in good]), oe, "finite chunks' ef")
+    # The records of the non-finite chunks still have 12-bit fields, so an
+    # aggregate of them stays inside its own chunks: guards around out intact.
+    obuf = torch.full((n + 2 * G,), float(sentinel), dtype=torch.float32, device=dev)
+    note("non-finite chunks: sl_aggregate of their records")
+    sl.sl_aggregate([payload.contiguous()], [scales.contiguous()], obuf[G:G + n])
+    torch.cuda.synchronize()
+    ob = obuf.cpu().numpy()
+    assert (ob[:G].view(np.uint32) == sentinel.view(np.uint32)).all()
+    assert (ob[G + n:].view(np.uint32) == sentinel.view(np.uint32)).all()
