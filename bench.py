@@ -279,7 +279,69 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     flags_all = torch.empty((N_PEERS, n // CHUNK), dtype=torch.uint8, device=delta.device)
     t = timed(lambda: sl.sl_validate_payloads(peer_p, peer_s, flags_all))
     res["validate_24_peers"] = kstats(t, N_PEERS * (RECORD + 1) / CHUNK)
+    res["small_round_1m"] = small_round(sl, delta.device)
     return res
+
+
+def small_round(sl, dev, reps=50):
+    """A whole round at the 1,048,576-parameter shape (256 chunks), where
+    launches dominate: validate 24 peers, fused aggregate + update, compress.
+    Timed eagerly (back to back, as a caller would issue it) and as one HIP
+    graph replay."""
+    import torch
+
+    from communication_efficient_distributed_amd import datagen
+
+    W = datagen.SMALL_1M
+    n = datagen.WORKLOAD_PARAMS[W]
+    C = n // CHUNK
+    scratch = torch.zeros(n, dtype=torch.float32, device=dev)
+    pp, ps = [], []
+    for p in range(1, N_PEERS + 1):
+        scratch.zero_()
+        a, b = sl.compress(datagen.lognormal(n, W, p, 0, dev), scratch, BETA)
+        pp.append(a)
+        ps.append(b)
+    delta = datagen.lognormal(n, W, 0, 0, dev)
+    ef = torch.zeros(n, dtype=torch.float32, device=dev)
+    theta = datagen.theta0(n, W, dev)
+    payload = torch.empty((C, 112), dtype=torch.uint8, device=dev)
+    scales = torch.empty(C, dtype=torch.float32, device=dev)
+    flags = torch.empty((N_PEERS, C), dtype=torch.uint8, device=dev)
+
+    def round_():
+        sl.sl_validate_payloads(pp, ps, flags)
+        sl.sl_aggregate_apply(pp, ps, theta)
+        sl.sl_compress(delta, ef, BETA, payload, scales)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            round_()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        round_()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) / reps * 1e3
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        round_()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) / reps * 1e3
+    return {"params": n, "peers": N_PEERS, "kernels_per_round": 3,
+            "eager_us_per_round": round(eager_us, 2), "graph_us_per_round": round(graph_us, 2)}
 
 
 def host_cpu_model() -> str:
