@@ -372,18 +372,24 @@ def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
         ps = [s[:S].cpu().numpy() for s in peer_s]
         t0 = time.perf_counter()
         oracle.compress(d, e, beta=BETA, nthreads=T, inplace=True)
+        t1 = time.perf_counter()
         oracle.aggregate(pp, ps, m, nthreads=T)
-        return m, time.perf_counter() - t0
+        t2 = time.perf_counter()
+        return m, t2 - t0, t1 - t0, t2 - t1
 
     S = min(args.cpu_sample_chunks, n // CHUNK)
     T = max(1, min(16, os.cpu_count() or 1))
-    m, dt = run(S, T)
+    m, dt, dc, da = run(S, T)
     S1 = min(4096, S)
-    m1, dt1 = run(S1, 1)
-    return {"value": round(m / dt / 1e9, 5), "unit": "Gparams/s", "cores": T, "kind": "oracle",
+    m1, dt1, dc1, da1 = run(S1, 1)
+    g = lambda params, sec: round(params / sec / 1e9, 5)
+    return {"value": g(m, dt), "unit": "Gparams/s", "cores": T, "kind": "oracle",
             "sample": f"first {S} chunks ({m} params) of the same workload: compress + "
                       f"aggregate {N_PEERS} peers, {dt:.2f} s wall on {T} threads",
-            "single_thread": {"value": round(m1 / dt1 / 1e9, 5), "unit": "Gparams/s",
+            "compress_gparams_per_s": g(m, dc), "aggregate_gparams_per_s": g(m, da),
+            "single_thread": {"value": g(m1, dt1), "unit": "Gparams/s",
+                              "compress_gparams_per_s": g(m1, dc1),
+                              "aggregate_gparams_per_s": g(m1, da1),
                               "sample": f"first {S1} chunks, {dt1:.2f} s wall on 1 thread"},
             "host_cpu": host_cpu_model(), "host_cpus_visible": os.cpu_count()}
 

@@ -131,7 +131,8 @@ sl_status sl_compress_weights(const float* theta_pre, const float* theta_post, f
  * Payloads are trusted: malformed records (non-increasing indices, negative or
  * non-finite scales) give unspecified values but every access stays inside the
  * chunk's own 4096 outputs, since a 12-bit field cannot leave the chunk.  Use
- * sl_validate_payload for records from untrusted peers.
+ * sl_validate_payloads (or sl_validate_payload) for records from untrusted
+ * peers.
  */
 sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scales,
                        int32_t n_peers, float* out, int64_t n, void* stream);
