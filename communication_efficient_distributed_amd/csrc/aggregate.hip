@@ -3,8 +3,8 @@
 //
 // "The Sparse Frontier: SparseLoCo and the Compression Math Behind
 // Permissionless Pre-Training", section "Why Extreme Sparsity Doesn't Break
-// Convergence", paragraph "Sparse aggregation can improve model quality": the
-// receivers combine the union of the peers' selected coordinates.  The sum is
+// Convergence", sparse-aggregation paragraph: the receivers combine the union
+// of the peers' selected coordinates.  The sum is
 // accumulated from +0.0 in ascending peer order for every coordinate.
 //
 // Mapping: one 64-lane wavefront owns one output chunk and a 16 KiB LDS tile of

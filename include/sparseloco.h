@@ -114,9 +114,9 @@ sl_status sl_compress_weights(const float* theta_pre, const float* theta_post, f
 /*
  * sl_aggregate -- decode n_peers payloads and sum them into a dense update.
  *
- * [SF] "Why Extreme Sparsity Doesn't Break Convergence", paragraph "Sparse
- * aggregation can improve model quality": the receivers combine the union of
- * the peers' selected coordinates.  Reading: the result is the plain sum,
+ * [SF] "Why Extreme Sparsity Doesn't Break Convergence", sparse-aggregation
+ * paragraph: the receivers combine the union of the peers' selected
+ * coordinates.  Reading: the result is the plain sum,
  * accumulated from +0.0 in ascending peer order for every coordinate, in fp32
  * with round-to-nearest-even.  out[i] is +0.0 where no peer selected i.
  *

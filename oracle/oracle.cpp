@@ -21,8 +21,8 @@
  *   6. 64 x (2 + 12) bits = 112 bytes per chunk       [SF, the per-chunk layout
  *                                                    formula after lever 3]
  *   7. residual back into ef                          [SF, error-feedback paragraph]
- *   8. receivers sum the union of peers' entries      [SF, "Sparse aggregation
- *                                                    can improve model quality"]
+ *   8. receivers sum the union of peers' entries      [SF, sparse-aggregation
+ *                                                    paragraph]
  *
  * Readings (the pages leave these open; each is stated where it is used):
  *   R1 beta is a parameter; beta = 1 is the pages' plain accumulation.

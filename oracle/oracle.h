@@ -14,9 +14,9 @@
  *          parameters, top-64 by absolute magnitude, four 2-bit levels with a
  *          per-chunk scale, 12-bit in-chunk indices, 64 x 14 bits = 112 bytes
  *          per chunk, 146.3x versus fp32.
- *        - "Why Extreme Sparsity Doesn't Break Convergence", paragraph "Error
- *          feedback accumulation": what is not sent rolls into the next round.
- *        - same section, paragraph "Sparse aggregation": receivers sum the
+ *        - "Why Extreme Sparsity Doesn't Break Convergence", error-feedback
+ *          paragraph: what is not sent rolls into the next round.
+ *        - same section, sparse-aggregation paragraph: receivers sum the
  *          union of the peers' selected coordinates.
  *  [CV]  "Covenant-72B: Decentralized Training is No Longer Just a Dream"
  *        (wispaper.ai), "SparseLoCo: Breaking the Bandwidth Barrier".

@@ -1,8 +1,8 @@
 """Pins of the oracle's aggregator, outer update and payload validator.
 
-"Sparse aggregation can improve model quality" (The Sparse Frontier, section
-"Why Extreme Sparsity Doesn't Break Convergence"): receivers sum the union of
-the peers' selected coordinates.
+The Sparse Frontier, section "Why Extreme Sparsity Doesn't Break Convergence",
+sparse-aggregation paragraph: receivers sum the union of the peers' selected
+coordinates.
 """
 from fractions import Fraction
 
