@@ -222,7 +222,7 @@ def main():
             "compress_plus_aggregate": kstats(tc + ta, BYTES_COMPRESS + BYTES_AGGREGATE),
         },
         "wall_s_timed": round(wall, 4),
-        "device": torch.cuda.get_device_name(dev),
+        "device": device_props(torch, dev),
     }
 
     if not args.no_next_rows:
@@ -342,6 +342,13 @@ def small_round(sl, dev, reps=50):
     graph_us = e0.elapsed_time(e1) / reps * 1e3
     return {"params": n, "peers": N_PEERS, "kernels_per_round": 3,
             "eager_us_per_round": round(eager_us, 2), "graph_us_per_round": round(graph_us, 2)}
+
+
+def device_props(torch, dev) -> dict:
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1)}
 
 
 def host_cpu_model() -> str:
