@@ -286,8 +286,9 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
 def small_round(sl, dev, reps=50):
     """A whole round at the 1,048,576-parameter shape (256 chunks), where
     launches dominate: validate 24 peers, fused aggregate + update, compress.
-    Timed eagerly (back to back, as a caller would issue it) and as one HIP
-    graph replay."""
+    Timed eagerly (back to back, as a caller would issue it), eagerly with
+    the peers' pointer tables prepared once (PeerSet), and as one HIP graph
+    replay."""
     import torch
 
     from communication_efficient_distributed_amd import datagen
@@ -328,6 +329,22 @@ def small_round(sl, dev, reps=50):
     e1.record()
     torch.cuda.synchronize()
     eager_us = e0.elapsed_time(e1) / reps * 1e3
+    peers = sl.PeerSet(pp, ps)                   # pointer tables checked and built once
+
+    def round_peerset():
+        sl.sl_validate_payloads(peers, None, flags)
+        sl.sl_aggregate_apply(peers, None, theta)
+        sl.sl_compress(delta, ef, BETA, payload, scales)
+
+    for _ in range(3):
+        round_peerset()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        round_peerset()
+    e1.record()
+    torch.cuda.synchronize()
+    peerset_us = e0.elapsed_time(e1) / reps * 1e3
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         round_()
@@ -341,7 +358,9 @@ def small_round(sl, dev, reps=50):
     torch.cuda.synchronize()
     graph_us = e0.elapsed_time(e1) / reps * 1e3
     return {"params": n, "peers": N_PEERS, "kernels_per_round": 3,
-            "eager_us_per_round": round(eager_us, 2), "graph_us_per_round": round(graph_us, 2)}
+            "eager_us_per_round": round(eager_us, 2),
+            "eager_peerset_us_per_round": round(peerset_us, 2),
+            "graph_us_per_round": round(graph_us, 2)}
 
 
 def device_props(torch, dev) -> dict:

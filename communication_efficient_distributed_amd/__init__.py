@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     SL_PAYLOAD_BYTES,
     SL_TOPK,
     LibraryMissing,
+    PeerSet,
     SparseLoCoError,
     aggregate,
     compress,

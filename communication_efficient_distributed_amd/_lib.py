@@ -188,6 +188,8 @@ def sl_validate_payloads(payloads, scales, flags: torch.Tensor, stream=None) -> 
     N = len(payloads)
     if flags.dim() != 2 or flags.shape[0] != N:
         raise ValueError("flags must be a [n_peers, n_chunks] tensor")
+    if isinstance(payloads, PeerSet) and payloads.device is not None and flags.device != payloads.device:
+        raise ValueError("flags must be on the peers' device")
     C = flags.shape[1]
     N, pa, sa, _keep = _peer_arrays(payloads, scales, C)
     f = _dev(flags, "flags", torch.uint8)
@@ -197,8 +199,46 @@ def sl_validate_payloads(payloads, scales, flags: torch.Tensor, stream=None) -> 
                                                                    _stream_of(flags, stream)))
 
 
+class PeerSet:
+    """The peers' record and scale tensors, checked once, with the C pointer
+    tables kept for repeated calls (receive buffers reused round after round).
+    Pass it as `payloads` (with `scales=None`) to sl_aggregate,
+    sl_aggregate_apply, aggregate and sl_validate_payloads.  The tensors are
+    held, so their storage stays alive; their contents may change between
+    calls, their storage must not be replaced."""
+
+    def __init__(self, payloads, scales):
+        payloads, scales = list(payloads), list(scales)
+        if len(payloads) != len(scales):
+            raise ValueError("payloads and scales lists differ in length")
+        if len(payloads) > SL_MAX_PEERS:
+            raise ValueError(f"at most {SL_MAX_PEERS} peers")
+        C = scales[0].numel() if scales else 0
+        self.n_peers = len(payloads)
+        self.n_chunks = C
+        self.device = payloads[0].device if payloads else None
+        pp = (ctypes.c_void_p * max(self.n_peers, 1))()
+        sp = (ctypes.c_void_p * max(self.n_peers, 1))()
+        for p in range(self.n_peers):
+            if payloads[p].numel() != C * SL_PAYLOAD_BYTES or scales[p].numel() != C:
+                raise ValueError(f"peer {p}: payload/scales sizes differ from peer 0's")
+            pp[p] = _dev(payloads[p], f"payloads[{p}]", torch.uint8).value
+            sp[p] = _dev(scales[p], f"scales[{p}]", torch.float32).value
+        self._tensors = (payloads, scales)
+        self._arrays = (pp, sp)
+        self.pa = ctypes.cast(pp, ctypes.c_void_p)
+        self.sa = ctypes.cast(sp, ctypes.c_void_p)
+
+    def __len__(self):
+        return self.n_peers
+
+
 def _peer_arrays(payloads, scales, C):
-    if len(payloads) != len(scales):
+    if isinstance(payloads, PeerSet):
+        if payloads.n_peers and payloads.n_chunks != C:
+            raise ValueError("peer records do not match the dense buffer")
+        return payloads.n_peers, payloads.pa, payloads.sa, payloads
+    if scales is None or len(payloads) != len(scales):
         raise ValueError("payloads and scales lists differ in length")
     N = len(payloads)
     pp = (ctypes.c_void_p * max(N, 1))()
@@ -253,12 +293,17 @@ def compress(delta: torch.Tensor, ef: torch.Tensor, beta: float = 0.95, stream=N
     return payload, scales
 
 
-def aggregate(payloads, scales, n: int | None = None, out: torch.Tensor | None = None,
+def aggregate(payloads, scales=None, n: int | None = None, out: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:
     if out is None:
-        if n is None:
-            n = payloads[0].numel() // SL_PAYLOAD_BYTES * SL_CHUNK
-        dev = payloads[0].device if payloads else torch.device("cuda")
+        if isinstance(payloads, PeerSet):
+            if n is None:
+                n = payloads.n_chunks * SL_CHUNK
+            dev = payloads.device or torch.device("cuda")
+        else:
+            if n is None:
+                n = payloads[0].numel() // SL_PAYLOAD_BYTES * SL_CHUNK
+            dev = payloads[0].device if payloads else torch.device("cuda")
         out = torch.empty(n, dtype=torch.float32, device=dev)
     sl_aggregate(payloads, scales, out, stream)
     return out

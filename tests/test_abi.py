@@ -239,3 +239,13 @@ def test_validate_many_argument_checks(lib):
     assert call(pp, ss, 3, flags=pp[1] + 16) == SL_ERR_INVALID_ARG      # flags overlap a record
     assert call(pp, ss, 3, flags=ss[2] - 8) == SL_ERR_INVALID_ARG       # flags (48 bytes) reach a scale buffer
     assert lib.sl_validate_payloads(None, None, 2, 16, F, None) == SL_ERR_INVALID_ARG
+
+
+def test_peerset_checks_once_and_rejects_bad_tensors():
+    import communication_efficient_distributed_amd as sl
+    with pytest.raises(ValueError):
+        sl.PeerSet([torch.zeros((4, 112), dtype=torch.uint8)], [torch.zeros(4)])      # host tensors
+    with pytest.raises(ValueError):
+        sl.PeerSet([torch.zeros((4, 112), dtype=torch.uint8)], [])                     # lengths differ
+    empty = sl.PeerSet([], [])
+    assert len(empty) == 0 and empty.n_chunks == 0

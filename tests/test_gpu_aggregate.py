@@ -218,3 +218,35 @@ def test_ragged_chunk_counts(orc, n_peers, n_chunks):
     sl.sl_aggregate_apply(to_gpu(payloads), to_gpu(scales), t)
     torch.cuda.synchronize()
     assert_bitwise(t.cpu().numpy(), orc.apply_mean(theta, o, n_peers), "fused")
+
+
+def test_peerset_matches_lists_and_follows_buffer_contents(orc):
+    """A PeerSet built once serves aggregate, fused update and validation, and
+    sees new record contents written into the same buffers between calls."""
+    sl = require_gpu()
+    n_chunks, N = 40, 24
+    n = n_chunks * 4096
+    pl1, sc1 = random_peers(orc, N, n_chunks, seed=31)
+    pl2, sc2 = random_peers(orc, N, n_chunks, seed=32)
+    dp, ds = to_gpu(pl1), to_gpu(sc1)
+    peers = sl.PeerSet(dp, ds)
+    note("PeerSet: aggregate, fused, validate")
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    sl.sl_aggregate(peers, None, out)
+    torch.cuda.synchronize()
+    assert_bitwise(out.cpu().numpy(), orc.aggregate(pl1, sc1, n), "aggregate via PeerSet")
+    for p in range(N):                                   # new round, same receive buffers
+        dp[p].copy_(torch.from_numpy(pl2[p]))
+        ds[p].copy_(torch.from_numpy(sc2[p]))
+    got = sl.aggregate(peers)
+    torch.cuda.synchronize()
+    want2 = orc.aggregate(pl2, sc2, n)
+    assert_bitwise(got.cpu().numpy(), want2, "aggregate after buffer refill")
+    theta = datagen.theta0(n, datagen.SMALL_1M).numpy()
+    t = torch.from_numpy(theta.copy()).cuda()
+    sl.sl_aggregate_apply(peers, None, t)
+    flags = torch.full((N, n_chunks), 255, dtype=torch.uint8, device="cuda")
+    sl.sl_validate_payloads(peers, None, flags)
+    torch.cuda.synchronize()
+    assert_bitwise(t.cpu().numpy(), orc.apply_mean(theta, want2, N), "fused via PeerSet")
+    assert not flags.cpu().numpy().any()
