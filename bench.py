@@ -381,6 +381,39 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
+def oracle_per_workload(T, sample_chunks=2048):
+    """The oracle's compress and 24-peer aggregate rates on a 2048-chunk
+    sample of each workload's own distribution (host-generated inputs, peers
+    compressed by the oracle from ef = 0), plus the time the whole of each
+    workload would take at that rate (extrapolated, per chunk)."""
+    import numpy as np
+
+    import oracle
+    from communication_efficient_distributed_amd import datagen
+
+    m = sample_chunks * CHUNK
+    res = {}
+    for name, W in (("small_1m", datagen.SMALL_1M), ("attn_8192", datagen.ATTN_8192),
+                    ("mlp_8192x28672", datagen.MLP_8192x28672),
+                    ("decoder_block", datagen.DECODER_BLOCK), ("flat_16b", datagen.FLAT_16B)):
+        full = datagen.WORKLOAD_PARAMS[W]
+        k = min(m, full)
+        d = datagen.workload_delta(W, 0, 0, n=k).numpy()
+        peers = [oracle.compress(datagen.workload_delta(W, p, 0, n=k).numpy(), np.zeros(k, np.float32),
+                                 beta=BETA, nthreads=T)[:2] for p in range(1, 4)]
+        pp = [peers[i % 3][0] for i in range(N_PEERS)]
+        ps = [peers[i % 3][1] for i in range(N_PEERS)]
+        t0 = time.perf_counter()
+        oracle.compress(d, np.zeros(k, np.float32), beta=BETA, nthreads=T)
+        t1 = time.perf_counter()
+        oracle.aggregate(pp, ps, k, nthreads=T)
+        t2 = time.perf_counter()
+        res[name] = {"sample_params": k, "compress_gparams_per_s": round(k / (t1 - t0) / 1e9, 5),
+                     "aggregate_gparams_per_s": round(k / (t2 - t1) / 1e9, 5),
+                     "full_workload_seconds_extrapolated": round(full / k * (t2 - t0), 2)}
+    return res
+
+
 def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
     """The CPU oracle on the first S chunks of the same workload, the same step
     (compress + 24-peer aggregate), on up to 16 host threads (and on one
@@ -409,7 +442,9 @@ def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
     S1 = min(4096, S)
     m1, dt1, dc1, da1 = run(S1, 1)
     g = lambda params, sec: round(params / sec / 1e9, 5)
+    per_workload = oracle_per_workload(T)
     return {"value": g(m, dt), "unit": "Gparams/s", "cores": T, "kind": "oracle",
+            "per_workload_sample": per_workload,
             "sample": f"first {S} chunks ({m} params) of the same workload: compress + "
                       f"aggregate {N_PEERS} peers, {dt:.2f} s wall on {T} threads",
             "compress_gparams_per_s": g(m, dc), "aggregate_gparams_per_s": g(m, da),
