@@ -29,6 +29,7 @@
 
 #include "internal.h"
 #include "record.h"
+#include "residency.h"
 #include "sparseloco.h"
 #include "wave.h"
 
@@ -230,24 +231,28 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
     finish_chunk<APPLY>(tile, dst_chunk, th, nf, lane);
 }
 
-// theta <- theta - out / n_peers over one 4096-element chunk per wavefront,
-// streaming loads and stores.
-__global__ __launch_bounds__(kWave) void apply_mean_kernel(float* theta, const float* out, float nf,
-                                                           int64_t n_chunks) {
-    const int lane = (int)threadIdx.x;
+// theta <- theta - out / n_peers.  One workgroup of four wavefronts per
+// 4096-element chunk, four float4 of each stream per lane, nontemporal loads
+// and stores.
+constexpr int kMeanWaves = 4;
+constexpr int kMeanSlots = SL_CHUNK / (4 * kWave * kMeanWaves);  // 4
+
+__global__ __launch_bounds__(kWave * kMeanWaves) void apply_mean_kernel(float* theta, const float* out, float nf,
+                                                                        int64_t n_chunks) {
+    const int tid = (int)threadIdx.x;
     const int64_t chunk = (int64_t)blockIdx.x;
     if (chunk >= n_chunks) return;
-    const size_t base = (size_t)chunk * SL_CHUNK;
-    v4f t[kSlots], o[kSlots];
+    const size_t base = (size_t)chunk * SL_CHUNK + 4 * (size_t)tid;
+    v4f t[kMeanSlots], o[kMeanSlots];
 #pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
-        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+    for (int m = 0; m < kMeanSlots; ++m) {
+        const size_t off = base + (size_t)(4 * kWave * kMeanWaves) * m;
         t[m] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(theta + off));
         o[m] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(out + off));
     }
 #pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
-        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+    for (int m = 0; m < kMeanSlots; ++m) {
+        const size_t off = base + (size_t)(4 * kWave * kMeanWaves) * m;
         v4f r;
         r.x = t[m].x - o[m].x / nf;
         r.y = t[m].y - o[m].y / nf;
@@ -256,6 +261,14 @@ __global__ __launch_bounds__(kWave) void apply_mean_kernel(float* theta, const f
         __builtin_nontemporal_store(r, reinterpret_cast<v4f*>(theta + off));
     }
 }
+
+// Residency cap of apply_mean (workgroups per CU, through unused dynamic
+// LDS).  On 8192 x 28672 parameters: 437-443 us at 2 or 3, 454-457 us at 4,
+// 463-466 us for the earlier one-wavefront-per-chunk kernel.  The aggregator
+// is left uncapped (9 workgroups per CU by its own LDS): capping it at 8 gained
+// 1%, at 6 or 4 it lost 11% and 52%.
+constexpr int kCapApplyMean = 3;
+static_assert(cap_is_exact(kCapApplyMean, 0), "residency cap");
 
 template <bool APPLY>
 hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float* dst,
@@ -293,8 +306,8 @@ hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, in
     int64_t n_chunks = n / SL_CHUNK;
     float nf = (float)n_peers;
     void* args[] = {(void*)&theta, (void*)&out, (void*)&nf, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&apply_mean_kernel),
-                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&apply_mean_kernel), dim3((unsigned)n_chunks),
+                           dim3(kWave * kMeanWaves), args, residency_lds(kCapApplyMean, 0), stream);
 }
 
 }  // namespace sl

@@ -7,16 +7,21 @@
 // 112-byte record, and the residual written back to the error-feedback buffer
 // (same page, "Why Extreme Sparsity Doesn't Break Convergence").
 //
-// Mapping: one 64-lane wavefront owns one chunk.  Lane l holds elements
-// 256*m + 4*l + j (m = 0..15, j = 0..3) in registers, so every global load and
-// store instruction of the wavefront touches one contiguous KiB.  The wavefront
-// has a private 8 KiB LDS slice; no barrier ties wavefronts together.
+// Mapping: one workgroup of four 64-lane wavefronts owns one chunk.
+// Wavefront w holds elements 1024 w + 256 m + 4 l + j (m, j = 0..3) in 16
+// registers per lane, so every global load and store instruction touches one
+// contiguous KiB.  The selection's partial results cross wavefronts through
+// 8 KiB of LDS and workgroup barriers; no barrier ties workgroups together.
+// (On 8192 x 28672 parameters four wavefronts per chunk measured 5% faster
+// than one, which needs 167 registers per lane and runs three wavefronts per
+// SIMD; two and eight wavefronts per chunk were slower than four.)
 //
 // Selection (exact, deterministic): find the 64th element of the order
 // (|acc| descending, index ascending) -- the "cut" -- by an MSB-first radix
 // select over the 31-bit magnitude key bits(acc) & 0x7fffffff:
 //   level 0  2048-bin LDS histogram of key bits 30..20 (exponent + 3 mantissa
-//            bits).  Exact zeros are counted with ballots instead of atomics.
+//            bits), shared by the four wavefronts.  Exact zeros are counted
+//            with ballots instead of atomics.
 //   then     if the boundary bin holds exactly the entries still needed, the
 //            cut is "key >= bin start"; if it holds at most 64 entries, they
 //            are compacted to LDS and ranked exactly by (key, index) with
@@ -27,31 +32,37 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "residency.h"
 #include "sparseloco.h"
 #include "wave.h"
 
 namespace sl {
 namespace {
 
-constexpr int kPerLane = SL_CHUNK / kWave;  // 64 elements per lane
-constexpr int kSlots = kPerLane / 4;        // 16 float4 per lane
-constexpr int kLdsWords = 2048;             // per wavefront
+constexpr int kWaves = 4;                      // wavefronts per chunk
+constexpr int kThreads = kWave * kWaves;
+constexpr int kPerLane = SL_CHUNK / kThreads;  // 16 elements per lane
+constexpr int kSlots = kPerLane / 4;           // 4 float4 per lane
+constexpr int kSpan = SL_CHUNK / kWaves;       // 1024 elements per wavefront
+constexpr int kLdsWords = 2048;
 constexpr uint32_t kKeyMask = 0x7fffffffu;
 constexpr uint32_t kSignBit = 0x80000000u;
 
-// Wavefronts per SIMD the register allocation is sized for.
-#ifndef SL_COMPRESS_WAVES_PER_EU
-#define SL_COMPRESS_WAVES_PER_EU 3
-#endif
-
 static_assert(SL_TOPK == kWave, "one kept entry per lane");
 static_assert(SL_INDEX_BITS == 12 && SL_CODE_BITS == 2, "payload layout");
+static_assert(SL_TOPK * kWaves + 128 + 64 + 64 <= kLdsWords, "entry segments and packing scratch fit");
+
+struct Shared {
+    uint32_t lds[kLdsWords];  // histograms, candidate list, index bitmap, entries
+    uint32_t part[kWaves];    // one count or maximum per wavefront
+    uint32_t cut[3];          // the cut, broadcast by wavefront 0
+};
 
 __device__ __forceinline__ uint32_t key_of(float v) { return __float_as_uint(v) & kKeyMask; }
 
-// In-chunk index of register slot q = 4*m + j of this lane.
-__device__ __forceinline__ uint32_t elem_index(int q, int lane) {
-    return (uint32_t)(256 * (q >> 2) + 4 * lane + (q & 3));
+// In-chunk index of register slot q = 4 m + j of lane `lane` in wavefront w.
+__device__ __forceinline__ uint32_t elem_index(int w, int q, int lane) {
+    return (uint32_t)(kSpan * w + 256 * (q >> 2) + 4 * lane + (q & 3));
 }
 
 // The kept set is {x : key > key_cut} plus, when tie is set, the entries with
@@ -68,14 +79,15 @@ struct Boundary {
     uint32_t count;  // entries in the bin itself
 };
 
-__device__ __forceinline__ void clear_words(uint32_t* p, int words, int lane) {
+__device__ __forceinline__ void clear_shared(uint32_t* p, int words, int tid) {
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    for (int w = lane * 4; w < words; w += kWave * 4) *reinterpret_cast<uint4*>(p + w) = z;
+    for (int i = tid * 4; i < words; i += kThreads * 4) *reinterpret_cast<uint4*>(p + i) = z;
 }
 
 // Bin d with count(bins > d) < need <= count(bins >= d).  Lane l owns bins
 // [l*B, l*B + B); each lane reads its bins starting at a lane-dependent
-// rotation so that the 16-byte reads spread over the LDS banks.
+// rotation so that the 16-byte reads spread over the LDS banks.  Every
+// wavefront computes the same answer from the same histogram.
 template <int B>
 __device__ __forceinline__ Boundary find_boundary(const uint32_t* hist, uint32_t need, int lane) {
     static_assert(B % 4 == 0 && ((B / 4) & (B / 4 - 1)) == 0, "bins per lane");
@@ -105,12 +117,22 @@ __device__ __forceinline__ Boundary find_boundary(const uint32_t* hist, uint32_t
     return b;
 }
 
+// The cut written by wavefront 0, read by every wavefront after a barrier.
+__device__ __forceinline__ Cut broadcast_cut(const Shared& sh) {
+    __syncthreads();
+    Cut c;
+    c.key = sh.cut[0];
+    c.idx = sh.cut[1];
+    c.tie = sh.cut[2] != 0u;
+    return c;
+}
+
 // Histogram of key bits [SHIFT, SHIFT+10) over entries whose resolved bits
 // match prefix.  A slot where every matching lane falls in the same bin adds
 // its count with one atomic (heavy ties, e.g. many exact zeros).
 template <int SHIFT>
-__device__ __forceinline__ void refine_histogram(const float (&acc)[kPerLane], uint32_t* hist,
-                                 uint32_t pmask, uint32_t prefix, int lane) {
+__device__ __forceinline__ void refine_histogram(const float (&acc)[kPerLane], uint32_t* hist, uint32_t pmask,
+                                                 uint32_t prefix, int lane) {
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         const uint32_t k = key_of(acc[q]);
@@ -122,22 +144,28 @@ __device__ __forceinline__ void refine_histogram(const float (&acc)[kPerLane], u
             const uint32_t b0 = read_lane(bin, first);
             const uint64_t same = ballot(c && bin == b0);
             if (same == bm) {
-                if (lane == first) lds_add(&hist[b0], (uint32_t)__popcll(bm));
+                if (lane == first) block_lds_add(&hist[b0], (uint32_t)__popcll(bm));
             } else if (c) {
-                lds_add(&hist[bin], 1u);
+                block_lds_add(&hist[bin], 1u);
             }
         }
     }
 }
 
-// At most 64 candidates (resolved bits == prefix): rank them exactly by
-// (key descending, index ascending) and return the one at position need-1.
-// Candidates share the resolved bits, so (low key bits, 4095 - index) fits
-// one 32-bit sort word.
-__device__ __forceinline__ Cut rank_cut(const float (&acc)[kPerLane], uint32_t* list, uint32_t pmask,
-                        uint32_t prefix, uint32_t lowmask, uint32_t need, uint32_t cnt,
-                        int lane) {
+// At most 64 candidates (resolved bits == prefix) across the four wavefronts:
+// compact them into one LDS list (wavefront w after those of wavefronts < w),
+// rank them in wavefront 0 by (key descending, index ascending) and broadcast
+// the one at position need-1.  Candidates share the resolved bits, so (low
+// key bits, 4095 - index) fits one 32-bit sort word.
+__device__ __forceinline__ Cut rank_cut(const float (&acc)[kPerLane], Shared& sh, uint32_t pmask, uint32_t prefix,
+                                        uint32_t lowmask, uint32_t need, uint32_t cnt, int w, int lane) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) mine += (uint32_t)__popcll(ballot((key_of(acc[q]) & pmask) == prefix));
+    if (lane == 0) sh.part[w] = mine;
+    __syncthreads();
     uint32_t base = 0;
+    for (int v = 0; v < w; ++v) base += sh.part[v];
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         const uint32_t k = key_of(acc[q]);
@@ -145,124 +173,132 @@ __device__ __forceinline__ Cut rank_cut(const float (&acc)[kPerLane], uint32_t* 
         const uint64_t bm = ballot(c);
         if (bm) {
             const uint32_t pos = base + lanes_below(bm);
-            if (c && pos < (uint32_t)kWave)
-                list[pos] = ((k & lowmask) << 12) | (4095u - elem_index(q, lane));
+            if (c && pos < (uint32_t)kWave) sh.lds[pos] = ((k & lowmask) << 12) | (4095u - elem_index(w, q, lane));
             base += (uint32_t)__popcll(bm);
         }
     }
-    wave_sync();
-    const bool mine = (uint32_t)lane < cnt;
-    const uint32_t sk = mine ? list[lane] : 0u;
-    uint32_t rank = 0;
-    for (uint32_t f = 0; f < cnt; ++f) rank += read_lane(sk, (int)f) > sk ? 1u : 0u;
-    const uint64_t hit = ballot(mine && rank == need - 1u);
-    const int wl = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
-    const uint32_t sk_cut = read_lane(sk, wl);
-    const uint64_t same = ballot(mine && (sk >> 12) == (sk_cut >> 12));
-    Cut cut;
-    cut.key = prefix | (sk_cut >> 12);
-    cut.idx = 4095u - (sk_cut & 4095u);
-    cut.tie = __popcll(same) > 1;
-    return cut;
+    __syncthreads();
+    if (w == 0) {
+        const bool mine_c = (uint32_t)lane < cnt;
+        const uint32_t sk = mine_c ? sh.lds[lane] : 0u;
+        uint32_t rank = 0;
+        for (uint32_t f = 0; f < cnt; ++f) rank += read_lane(sk, (int)f) > sk ? 1u : 0u;
+        const uint64_t hit = ballot(mine_c && rank == need - 1u);
+        const int wl = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+        const uint32_t sk_cut = read_lane(sk, wl);
+        const uint64_t same = ballot(mine_c && (sk >> 12) == (sk_cut >> 12));
+        if (lane == 0) {
+            sh.cut[0] = prefix | (sk_cut >> 12);
+            sh.cut[1] = 4095u - (sk_cut & 4095u);
+            sh.cut[2] = __popcll(same) > 1 ? 1u : 0u;
+        }
+    }
+    return broadcast_cut(sh);
 }
 
-// More than 64 entries share the exact key K: the cut is the need-th smallest
-// index among them, found from a 4096-bit LDS bitmap.
-__device__ __forceinline__ Cut index_cut(const float (&acc)[kPerLane], uint32_t* bm, uint32_t K,
-                         uint32_t need, int lane) {
-    reinterpret_cast<uint2*>(bm)[lane] = make_uint2(0u, 0u);
-    wave_sync();
+// More than 64 entries share the exact key K: a 4096-bit LDS bitmap of their
+// indices from all four wavefronts; wavefront 0 finds the need-th smallest.
+__device__ __forceinline__ Cut index_cut(const float (&acc)[kPerLane], Shared& sh, uint32_t K, uint32_t need,
+                                         int w, int lane, int tid) {
+    if (tid < kWave) reinterpret_cast<uint2*>(sh.lds)[tid] = make_uint2(0u, 0u);
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         if (key_of(acc[q]) == K) {
-            const uint32_t i = elem_index(q, lane);
-            lds_or(&bm[i >> 5], 1u << (i & 31));
+            const uint32_t i = elem_index(w, q, lane);
+            block_lds_or(&sh.lds[i >> 5], 1u << (i & 31));
         }
     }
-    wave_sync();
-    const uint2 wv = reinterpret_cast<const uint2*>(bm)[lane];  // indices [64l, 64l+64)
-    const uint64_t w = ((uint64_t)wv.y << 32) | wv.x;
-    const uint32_t c = (uint32_t)__popcll(w);
-    const uint32_t incl = wave_prefix_sum(c, lane);
-    const uint64_t reach = ballot(incl >= need);
-    const int L = reach ? __ffsll((unsigned long long)reach) - 1 : 0;
-    const uint32_t r = need - (read_lane(incl, L) - read_lane(c, L));  // 1..64
-    uint64_t wl = ((uint64_t)read_lane(wv.y, L) << 32) | read_lane(wv.x, L);
-    for (uint32_t i = 1; i < r && i < 64u; ++i) wl &= wl - 1;
-    Cut cut;
-    cut.key = K;
-    cut.idx = 64u * (uint32_t)L + (uint32_t)__builtin_ctzll(wl);
-    cut.tie = true;
-    return cut;
+    __syncthreads();
+    if (w == 0) {
+        const uint2 wv = reinterpret_cast<const uint2*>(sh.lds)[lane];  // indices [64l, 64l+64)
+        const uint64_t wd = ((uint64_t)wv.y << 32) | wv.x;
+        const uint32_t c = (uint32_t)__popcll(wd);
+        const uint32_t incl = wave_prefix_sum(c, lane);
+        const uint64_t reach = ballot(incl >= need);
+        const int L = reach ? __ffsll((unsigned long long)reach) - 1 : 0;
+        const uint32_t r = need - (read_lane(incl, L) - read_lane(c, L));  // 1..64
+        uint64_t wl = ((uint64_t)read_lane(wv.y, L) << 32) | read_lane(wv.x, L);
+        for (uint32_t i = 1; i < r && i < 64u; ++i) wl &= wl - 1;
+        if (lane == 0) {
+            sh.cut[0] = K;
+            sh.cut[1] = 64u * (uint32_t)L + (uint32_t)__builtin_ctzll(wl);
+            sh.cut[2] = 1u;
+        }
+    }
+    return broadcast_cut(sh);
 }
 
-__device__ __forceinline__ Cut select_cut(const float (&acc)[kPerLane], uint32_t* lds, uint32_t mx, int lane) {
-    if (mx == 0u) {
-        Cut cut;  // all keys are 0: the lower-index rule keeps 0..63
+// Every wavefront returns the same cut; every path ends with a workgroup
+// barrier, after which the LDS may be reused.
+__device__ __forceinline__ Cut select_cut(const float (&acc)[kPerLane], Shared& sh, uint32_t mx, int w, int lane,
+                                          int tid) {
+    Cut cut;
+    cut.idx = 0u;
+    cut.tie = false;
+    if (mx == 0u) {  // all keys are 0: the lower-index rule keeps 0..63
         cut.key = 0u;
         cut.idx = 63u;
         cut.tie = true;
+        __syncthreads();
         return cut;
     }
     // Level 0: key bits 30..20.
-    clear_words(lds, kLdsWords, lane);
-    wave_sync();
+    clear_shared(sh.lds, kLdsWords, tid);
+    __syncthreads();
     uint32_t zeros = 0;
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         const uint32_t k = key_of(acc[q]);
         const bool nz = k != 0u;
         zeros += (uint32_t)(kWave - __popcll(ballot(nz)));
-        if (nz) lds_add(&lds[k >> 20], 1u);
+        if (nz) block_lds_add(&sh.lds[k >> 20], 1u);
     }
-    if (lane == 0 && zeros) lds_add(&lds[0], zeros);
-    wave_sync();
-    Boundary b = find_boundary<kLdsWords / kWave>(lds, (uint32_t)SL_TOPK, lane);
+    if (lane == 0 && zeros) block_lds_add(&sh.lds[0], zeros);
+    __syncthreads();
+    Boundary b = find_boundary<kLdsWords / kWave>(sh.lds, (uint32_t)SL_TOPK, lane);
     uint32_t need = (uint32_t)SL_TOPK - b.above;
     uint32_t prefix = b.digit << 20;
     uint32_t pmask = 0x7ff00000u;
-    Cut cut;
-    cut.idx = 0u;
-    cut.tie = false;
+    __syncthreads();  // every wavefront has read the histogram
     if (b.count == need) {
         cut.key = prefix;
         return cut;
     }
-    wave_sync();
-    if (b.count <= (uint32_t)kWave) return rank_cut(acc, lds, pmask, prefix, 0x000fffffu, need, b.count, lane);
+    if (b.count <= (uint32_t)kWave) return rank_cut(acc, sh, pmask, prefix, 0x000fffffu, need, b.count, w, lane);
 
     // Level 1: key bits 19..10 of the boundary bin.
-    clear_words(lds, 1024, lane);
-    wave_sync();
-    refine_histogram<10>(acc, lds, pmask, prefix, lane);
-    wave_sync();
-    b = find_boundary<1024 / kWave>(lds, need, lane);
+    clear_shared(sh.lds, 1024, tid);
+    __syncthreads();
+    refine_histogram<10>(acc, sh.lds, pmask, prefix, lane);
+    __syncthreads();
+    b = find_boundary<1024 / kWave>(sh.lds, need, lane);
     need -= b.above;
     prefix |= b.digit << 10;
     pmask = 0x7ffffc00u;
+    __syncthreads();
     if (b.count == need) {
         cut.key = prefix;
         return cut;
     }
-    wave_sync();
-    if (b.count <= (uint32_t)kWave) return rank_cut(acc, lds, pmask, prefix, 0x3ffu, need, b.count, lane);
+    if (b.count <= (uint32_t)kWave) return rank_cut(acc, sh, pmask, prefix, 0x3ffu, need, b.count, w, lane);
 
     // Level 2: key bits 9..0.
-    clear_words(lds, 1024, lane);
-    wave_sync();
-    refine_histogram<0>(acc, lds, pmask, prefix, lane);
-    wave_sync();
-    b = find_boundary<1024 / kWave>(lds, need, lane);
+    clear_shared(sh.lds, 1024, tid);
+    __syncthreads();
+    refine_histogram<0>(acc, sh.lds, pmask, prefix, lane);
+    __syncthreads();
+    b = find_boundary<1024 / kWave>(sh.lds, need, lane);
     need -= b.above;
     prefix |= b.digit;
     pmask = kKeyMask;
+    __syncthreads();
     if (b.count == need) {
         cut.key = prefix;
         return cut;
     }
-    wave_sync();
-    if (b.count <= (uint32_t)kWave) return rank_cut(acc, lds, pmask, prefix, 0u, need, b.count, lane);
-    return index_cut(acc, lds, prefix, need, lane);
+    if (b.count <= (uint32_t)kWave) return rank_cut(acc, sh, pmask, prefix, 0u, need, b.count, w, lane);
+    return index_cut(acc, sh, prefix, need, w, lane, tid);
 }
 
 // Smallest key k with 3 * value(k) > 2s, so that "magnitude bit set" is the
@@ -300,10 +336,12 @@ __device__ __forceinline__ void stream_store(float* p, float a, float b, float c
     __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
 }
 
+// Residual write-back of this wavefront's 1024 elements (ef_part points at
+// the first) and compaction of its kept entries (index | code << 12) into ent.
 template <bool TIE>
-__device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane], const Cut& cut,
-                                                   uint32_t kmag, uint32_t sbits, uint32_t s3bits,
-                                                   float* ef_chunk, uint32_t* ent, int lane) {
+__device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane], const Cut& cut, uint32_t kmag,
+                                                   uint32_t sbits, uint32_t s3bits, float* ef_part, uint32_t* ent,
+                                                   int w, int lane) {
     uint32_t nsel = 0;
 #pragma unroll
     for (int m = 0; m < kSlots; ++m) {
@@ -313,9 +351,8 @@ __device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane],
             const int q = 4 * m + j;
             const uint32_t bits = __float_as_uint(acc[q]);
             const uint32_t k = bits & kKeyMask;
-            const uint32_t idx = elem_index(q, lane);
-            const bool sel = TIE ? (k > cut.key || (k == cut.key && idx <= cut.idx))
-                                 : (k >= cut.key);
+            const uint32_t idx = elem_index(w, q, lane);
+            const bool sel = TIE ? (k > cut.key || (k == cut.key && idx <= cut.idx)) : (k >= cut.key);
             const bool mag = k >= kmag;
             const uint32_t dbits = (mag ? sbits : s3bits) | (bits & kSignBit);
             const float r = acc[q] - __uint_as_float(dbits);
@@ -323,86 +360,24 @@ __device__ __forceinline__ uint32_t write_residual(const float (&acc)[kPerLane],
             const uint64_t bm = ballot(sel);
             if (bm) {
                 const uint32_t pos = nsel + lanes_below(bm);
-                if (sel && pos < (uint32_t)SL_TOPK)
-                    ent[pos] = idx | ((((bits >> 31) << 1) | (mag ? 1u : 0u)) << 12);
+                if (sel && pos < (uint32_t)SL_TOPK) ent[pos] = idx | ((((bits >> 31) << 1) | (mag ? 1u : 0u)) << 12);
                 nsel += (uint32_t)__popcll(bm);
             }
         }
-        stream_store(ef_chunk + 4 * (m * kWave + lane), o[0], o[1], o[2], o[3]);
+        stream_store(ef_part + 4 * (m * kWave + lane), o[0], o[1], o[2], o[3]);
     }
     return nsel;
 }
 
-// acc = beta * ef + delta (one rounding) for the chunk starting at base.
-__device__ __forceinline__ void load_accumulator(const float* delta, const float* ef, float beta,
-                                                 size_t base, int lane, float (&acc)[kPerLane]) {
-#pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
-        const size_t off = base + 4 * (size_t)(m * kWave + lane);
-        const float4 dv = stream_load(delta + off);
-        const float4 ev = stream_load(ef + off);
-        acc[4 * m + 0] = __builtin_fmaf(beta, ev.x, dv.x);
-        acc[4 * m + 1] = __builtin_fmaf(beta, ev.y, dv.y);
-        acc[4 * m + 2] = __builtin_fmaf(beta, ev.z, dv.z);
-        acc[4 * m + 3] = __builtin_fmaf(beta, ev.w, dv.w);
-    }
-}
-
-// Pseudo-gradient formed on the fly: delta = theta_pre - theta_post (one fp32
-// subtraction; "Why DiLoCo Alone Isn't Enough" in "The Sparse Frontier" defines
-// the pseudo-gradient as the difference between the pre- and post-inner-loop
-// weights), then acc = beta * ef + delta with one rounding.
-__device__ __forceinline__ void load_accumulator_weights(const float* pre, const float* post,
-                                                         const float* ef, float beta, size_t base,
-                                                         int lane, float (&acc)[kPerLane]) {
-#pragma unroll
-    for (int m = 0; m < kSlots; ++m) {
-        const size_t off = base + 4 * (size_t)(m * kWave + lane);
-        const float4 a = stream_load(pre + off);
-        const float4 b = stream_load(post + off);
-        const float4 ev = stream_load(ef + off);
-        acc[4 * m + 0] = __builtin_fmaf(beta, ev.x, a.x - b.x);
-        acc[4 * m + 1] = __builtin_fmaf(beta, ev.y, a.y - b.y);
-        acc[4 * m + 2] = __builtin_fmaf(beta, ev.z, a.z - b.z);
-        acc[4 * m + 3] = __builtin_fmaf(beta, ev.w, a.w - b.w);
-    }
-}
-
-// Everything after the accumulator is formed: selection, scale, residual
-// write-back, ordering and packing of chunk `chunk`.
-__device__ __forceinline__ void compress_chunk(const float (&acc)[kPerLane], uint32_t* lds, float* ef,
-                                               uint8_t* payload, float* scales, int64_t chunk,
-                                               int lane) {
-    const size_t base = (size_t)chunk * SL_CHUNK;
-    uint32_t mx = 0;
-#pragma unroll
-    for (int q = 0; q < kPerLane; ++q) {
-        const uint32_t k = key_of(acc[q]);
-        mx = k > mx ? k : mx;
-    }
-    mx = uniform(wave_max(mx));
-
-    const Cut cut = select_cut(acc, lds, mx, lane);
-
-    // Scale and levels: s = max |acc| (= the largest kept magnitude).
-    const float s = __uint_as_float(mx);
-    const float s3 = s / 3.0f;
-    const uint32_t kmag = magnitude_threshold(s);
-
-    uint32_t* ent = lds;          // [0, 64)    kept entries, unordered
-    uint32_t* bmp = lds + 64;     // [64, 192)  4096-bit index bitmap
-    uint32_t* pre = lds + 192;    // [192, 256) per-64-index prefix counts
-    uint32_t* sorted = lds + 256; // [256, 320) kept entries in index order
-    wave_sync();
-    if (cut.tie)
-        write_residual<true>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, lane);
-    else
-        write_residual<false>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, lane);
-
-    // Order the 64 entries by index: counting sort through a bitmap.
+// Entry e (index | code << 12, one per lane, any order) of the 64 kept
+// entries: order them by index with a counting sort through a 4096-bit bitmap
+// and write the 112-byte record (24 dwords of 12-bit indices, then 4 dwords of
+// 2-bit codes).  bmp (128 words), pre (64) and sorted (64) are LDS scratch
+// that only the calling wavefront touches.
+__device__ __forceinline__ void order_and_pack(uint32_t e, uint32_t* bmp, uint32_t* pre, uint32_t* sorted,
+                                               uint8_t* record, int lane) {
     reinterpret_cast<uint2*>(bmp)[lane] = make_uint2(0u, 0u);
     wave_sync();
-    const uint32_t e = ent[lane];
     const uint32_t id = e & 4095u;
     lds_or(&bmp[id >> 5], 1u << (id & 31));
     wave_sync();
@@ -417,7 +392,6 @@ __device__ __forceinline__ void compress_chunk(const float (&acc)[kPerLane], uin
     wave_sync();
     const uint32_t es = sorted[lane];
 
-    // Pack: 24 dwords of 12-bit indices, then 4 dwords of 2-bit codes.
     uint32_t word = 0;
     if (lane < 24) {
         const int j0 = (32 * lane) / 12;
@@ -439,34 +413,93 @@ __device__ __forceinline__ void compress_chunk(const float (&acc)[kPerLane], uin
         word = spread16((uint32_t)(bmag >> (16 * q)) & 0xffffu) |
                (spread16((uint32_t)(bsgn >> (16 * q)) & 0xffffu) << 1);
     }
-    if (lane < SL_PAYLOAD_BYTES / 4)
-        reinterpret_cast<uint32_t*>(payload + (size_t)chunk * SL_PAYLOAD_BYTES)[lane] = word;
-    if (lane == 0) scales[chunk] = s;
-    wave_sync();   // the LDS slice is reused by the next chunk of this wavefront
+    if (lane < SL_PAYLOAD_BYTES / 4) reinterpret_cast<uint32_t*>(record)[lane] = word;
 }
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SL_COMPRESS_WAVES_PER_EU))) void compress_kernel(
-    const float* delta, float* ef, float beta, uint8_t* payload, float* scales, int64_t n_chunks) {
-    __shared__ __align__(16) uint32_t lds[kLdsWords];
-    const int lane = (int)threadIdx.x;
+// One chunk per workgroup.  WEIGHTS: the pseudo-gradient is formed on the fly
+// as a - b with one fp32 subtraction (a = theta_pre, b = theta_post; "Why
+// DiLoCo Alone Isn't Enough" in "The Sparse Frontier" defines it as the
+// difference between the pre- and post-inner-loop weights); otherwise a is
+// delta and b is unused.  Then acc = beta * ef + delta with one rounding.
+template <bool WEIGHTS>
+__global__ __launch_bounds__(kThreads) void compress_kernel(const float* a, const float* b, float* ef, float beta,
+                                                            uint8_t* payload, float* scales, int64_t n_chunks) {
+    __shared__ __align__(16) Shared sh;
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t chunk = (int64_t)blockIdx.x;
-    if (chunk >= n_chunks) return;
+    if (chunk >= n_chunks) return;  // the whole workgroup
+    const size_t base = (size_t)chunk * SL_CHUNK + (size_t)kSpan * (size_t)w;
     float acc[kPerLane];
-    load_accumulator(delta, ef, beta, (size_t)chunk * SL_CHUNK, lane, acc);
-    compress_chunk(acc, lds, ef, payload, scales, chunk, lane);
+#pragma unroll
+    for (int m = 0; m < kSlots; ++m) {
+        const size_t off = base + 4 * (size_t)(m * kWave + lane);
+        float4 dv = stream_load(a + off);
+        if constexpr (WEIGHTS) {
+            const float4 bv = stream_load(b + off);
+            dv = make_float4(dv.x - bv.x, dv.y - bv.y, dv.z - bv.z, dv.w - bv.w);
+        }
+        const float4 ev = stream_load(ef + off);
+        acc[4 * m + 0] = __builtin_fmaf(beta, ev.x, dv.x);
+        acc[4 * m + 1] = __builtin_fmaf(beta, ev.y, dv.y);
+        acc[4 * m + 2] = __builtin_fmaf(beta, ev.z, dv.z);
+        acc[4 * m + 3] = __builtin_fmaf(beta, ev.w, dv.w);
+    }
+
+    // Scale: s = max |acc| over the chunk (= the largest kept magnitude).
+    uint32_t mx = 0;
+#pragma unroll
+    for (int q = 0; q < kPerLane; ++q) {
+        const uint32_t k = key_of(acc[q]);
+        mx = k > mx ? k : mx;
+    }
+    mx = uniform(wave_max(mx));
+    if (lane == 0) sh.part[w] = mx;
+    __syncthreads();
+    for (int v = 0; v < kWaves; ++v) mx = sh.part[v] > mx ? sh.part[v] : mx;
+    __syncthreads();
+
+    const Cut cut = select_cut(acc, sh, mx, w, lane, tid);
+
+    const float s = __uint_as_float(mx);
+    const float s3 = s / 3.0f;
+    const uint32_t kmag = magnitude_threshold(s);
+    uint32_t* ent = sh.lds + SL_TOPK * w;  // this wavefront's kept entries
+    const uint32_t nsel =
+        cut.tie ? write_residual<true>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, w, lane)
+                : write_residual<false>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, w, lane);
+    if (lane == 0) sh.part[w] = nsel;
+    __syncthreads();
+    if (w == 0) {
+        // Entry j (0..63) of the chunk sits in the segment of the last
+        // wavefront whose entries start at or before j.
+        const uint32_t j = (uint32_t)lane;
+        uint32_t seg = 0, first = 0, start = 0;
+        for (int v = 0; v < kWaves; ++v) {
+            if (j >= start) {
+                seg = (uint32_t)v;
+                first = start;
+            }
+            start += sh.part[v];
+        }
+        const uint32_t e = sh.lds[SL_TOPK * seg + ((j - first) & (SL_TOPK - 1))];
+        uint32_t* bmp = sh.lds + SL_TOPK * kWaves;  // 128 words after the entry segments
+        uint32_t* pre = bmp + 128;                  // 64 words
+        uint32_t* sorted = pre + 64;                // 64 words
+        order_and_pack(e, bmp, pre, sorted, payload + (size_t)chunk * SL_PAYLOAD_BYTES, lane);
+        if (lane == 0) scales[chunk] = s;
+    }
 }
 
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SL_COMPRESS_WAVES_PER_EU))) void compress_weights_kernel(
-    const float* pre, const float* post, float* ef, float beta, uint8_t* payload, float* scales,
-    int64_t n_chunks) {
-    __shared__ __align__(16) uint32_t lds[kLdsWords];
-    const int lane = (int)threadIdx.x;
-    const int64_t chunk = (int64_t)blockIdx.x;
-    if (chunk >= n_chunks) return;
-    float acc[kPerLane];
-    load_accumulator_weights(pre, post, ef, beta, (size_t)chunk * SL_CHUNK, lane, acc);
-    compress_chunk(acc, lds, ef, payload, scales, chunk, lane);
-}
+// Residency caps (workgroups per CU, through unused dynamic LDS).  On
+// 8192 x 28672 parameters the weights variant, with three input streams, ran
+// 611-623 us uncapped (8 workgroups per CU) and 580-587 us at 4 or 5; the
+// compressor gained less from 6 (medians 461 -> 451 us; 4 or 5 lost 6%).
+constexpr int kCapCompress = 6;
+constexpr int kCapWeights = 5;
+static_assert(cap_is_exact(kCapCompress, sizeof(Shared)) && cap_is_exact(kCapWeights, sizeof(Shared)),
+              "residency caps");
 
 }  // namespace
 
@@ -475,16 +508,17 @@ hipError_t launch_compress_weights(const float* theta_pre, const float* theta_po
                                    hipStream_t stream) {
     void* args[] = {(void*)&theta_pre, (void*)&theta_post, (void*)&ef, (void*)&beta,
                     (void*)&payload, (void*)&scales, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_weights_kernel),
-                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel<true>), dim3((unsigned)n_chunks),
+                           dim3(kThreads), args, residency_lds(kCapWeights, sizeof(Shared)), stream);
 }
 
 hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* payload,
                            float* scales, int64_t n_chunks, hipStream_t stream) {
-    void* args[] = {(void*)&delta, (void*)&ef, (void*)&beta, (void*)&payload,
+    const float* unused = nullptr;
+    void* args[] = {(void*)&delta, (void*)&unused, (void*)&ef, (void*)&beta, (void*)&payload,
                     (void*)&scales, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel),
-                           dim3((unsigned)n_chunks), dim3(kWave), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel<false>), dim3((unsigned)n_chunks),
+                           dim3(kThreads), args, residency_lds(kCapCompress, sizeof(Shared)), stream);
 }
 
 }  // namespace sl

@@ -1,10 +1,10 @@
 // wave.h -- wavefront (64-lane) primitives for gfx950 used by the kernels.
 //
-// Every kernel in this library gives each wavefront its own chunk and its own
-// LDS slice, so the only synchronisation needed is inside one wavefront: LDS
-// instructions of a wavefront execute in issue order, and wave_sync() keeps the
-// compiler from moving LDS accesses across the point where lanes start reading
-// what other lanes wrote.
+// Inside one wavefront LDS instructions execute in issue order, and wave_sync()
+// keeps the compiler from moving LDS accesses across the point where lanes
+// start reading what other lanes wrote.  Kernels whose wavefronts share LDS
+// (the compressor's four wavefronts per chunk) use workgroup barriers and the
+// workgroup-scope atomics below.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,6 +76,16 @@ __device__ __forceinline__ void lds_add(uint32_t* p, uint32_t v) {
 
 __device__ __forceinline__ void lds_or(uint32_t* p, uint32_t v) {
     __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+}
+
+// LDS atomics at workgroup scope (several wavefronts update the same words;
+// ordering against other accesses comes from the barriers around them).
+__device__ __forceinline__ void block_lds_add(uint32_t* p, uint32_t v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ void block_lds_or(uint32_t* p, uint32_t v) {
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 }  // namespace sl

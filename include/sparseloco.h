@@ -20,7 +20,7 @@
  *  - Inputs must be finite: NaN and Inf are outside the contract (they are
  *    not detected and give unspecified codes, never out-of-bounds accesses).
  *  - Results do not depend on the launch configuration: each chunk is owned by
- *    one wavefront and no floating-point atomics are used, so repeated calls
+ *    one workgroup and no floating-point atomics are used, so repeated calls
  *    are bitwise identical.
  */
 #ifndef SPARSELOCO_H
