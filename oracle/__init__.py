@@ -45,6 +45,8 @@ def lib():
         L.orc_apply_mean.restype = ctypes.c_int
         L.orc_validate.argtypes = [P, P, i64, P]
         L.orc_validate.restype = ctypes.c_int64
+        L.orc_peer_stats.argtypes = [P, P, i64, P, P]
+        L.orc_peer_stats.restype = None
         L.orc_pseudo_gradient.argtypes = [P, P, i64, P]
         L.orc_pseudo_gradient.restype = None
         L.orc_decode.argtypes = [ctypes.c_uint8, f32]
@@ -158,6 +160,20 @@ def validate(payload, scales):
     bad = np.zeros(C, dtype=np.uint8)
     n_bad = lib().orc_validate(_ptr(payload), _ptr(scales), C, _ptr(bad))
     return int(n_bad), bad
+
+
+def peer_stats(payload, scales):
+    """Per-peer statistics of one peer's records: (counts int64[4], scale_max).
+    counts = [records flagged by validate, records with scale +-0, entries at
+    the magnitude level, entries with the sign bit]."""
+    payload = np.ascontiguousarray(payload, dtype=np.uint8).reshape(-1, PAYLOAD_BYTES)
+    scales = _f32(scales).reshape(-1)
+    C = payload.shape[0]
+    assert scales.size == C
+    counts = np.zeros(4, dtype=np.int64)
+    top = np.zeros(1, dtype=np.float32)
+    lib().orc_peer_stats(_ptr(payload), _ptr(scales), C, _ptr(counts), _ptr(top))
+    return counts, top[0]
 
 
 def pseudo_gradient(theta_pre, theta_post):

@@ -38,6 +38,11 @@
  *   R8 ef <- acc - decoded at kept positions, acc elsewhere.
  *   R9 aggregation returns the sum, from +0.0, peers in ascending order.
  *   R10 outer update theta <- theta - sum / N (correctly rounded division).
+ *   R11 per-peer statistics for anomaly screening ([SF], "What the Blockchain
+ *       Does (and Doesn't Do)": a crafted sparse update stands out to anomaly
+ *       detection): records flagged by the validator, records with a zero
+ *       scale, entries at the magnitude level, entries with the sign bit, and
+ *       the largest finite non-negative scale (-0 counts as +0).
  *
  * Parity status:
  *   orc_compress_unpacked  pinned (brute force over all inputs of tiny chunks,
@@ -51,6 +56,8 @@
  *                          the peer summation order is reading R9
  *   orc_apply_mean         pinned (closed form on exact inputs)
  *   orc_validate           pinned (hand-made malformed payloads, one per flag)
+ *   orc_peer_stats         pinned (counts of constructed records, bitwise
+ *                          reader of the code bytes, max over a numpy mask)
  *   orc_pseudo_gradient    pinned (exact small-integer weights)
  *   orc_decode             pinned (s/3 against exact-rational rounding)
  */
@@ -281,6 +288,34 @@ int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chun
         if (f) ++n_bad;
     }
     return n_bad;
+}
+
+void orc_peer_stats(const uint8_t* payload, const float* scales, int64_t n_chunks,
+                    int64_t* counts, float* scale_max) {
+    /* R11.  Flags as in orc_validate; the code counts take every record as
+     * received, well-formed or not. */
+    int64_t bad = 0, zero_scale = 0, magnitude = 0, negative = 0;
+    float top = 0.0f;
+    int32_t idx[kTopK];
+    uint8_t code[kTopK];
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        uint8_t f = 0;
+        orc_validate(payload + c * kPayloadBytes, scales + c, 1, &f);
+        if (f) ++bad;
+        const float s = scales[c];
+        if (s == 0.0f) ++zero_scale;
+        if ((f & 6u) == 0 && s > top) top = s;
+        unpack_one(payload + c * kPayloadBytes, idx, code);
+        for (int32_t j = 0; j < kTopK; ++j) {
+            if (code[j] & 1u) ++magnitude;
+            if (code[j] & 2u) ++negative;
+        }
+    }
+    counts[0] = bad;
+    counts[1] = zero_scale;
+    counts[2] = magnitude;
+    counts[3] = negative;
+    *scale_max = top;
 }
 
 void orc_pseudo_gradient(const float* theta_pre, const float* theta_post, int64_t n,

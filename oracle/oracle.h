@@ -75,6 +75,14 @@ int orc_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n);
 int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chunks,
                      uint8_t* bad);
 
+/* Statistics of one peer's n_chunks received records (reading R11):
+ * counts[0] records that orc_validate flags, counts[1] records whose scale is
+ * +0 or -0, counts[2] entries with code bit 0 (magnitude level), counts[3]
+ * entries with code bit 1 (sign); *scale_max = the largest scale among records
+ * whose scale is finite and not negative, +0 if there is none. */
+void orc_peer_stats(const uint8_t* payload, const float* scales, int64_t n_chunks,
+                    int64_t* counts, float* scale_max);
+
 /* Pseudo-gradient: delta[i] = theta_pre[i] - theta_post[i]. */
 void orc_pseudo_gradient(const float* theta_pre, const float* theta_post, int64_t n,
                          float* delta);

@@ -185,3 +185,52 @@ def test_bulk_record_generator_is_well_formed(orc):
     assert (idx[:, -1] == 4095).any() and (idx[:, 0] == 0).any()
     back, bc = orc.unpack(orc.pack(idx, code))
     assert np.array_equal(back, idx) and np.array_equal(bc, code)
+
+
+def test_peer_stats_of_constructed_records(orc):
+    """Per-peer statistics (reading of "What the Blockchain Does (and Doesn't
+    Do)" in The Sparse Frontier: a crafted sparse update stands out to anomaly
+    detection).  Expected counts come from the arrays the records were built
+    from and from a bitwise reader of the code bytes, not from the oracle."""
+    C = 40
+    idx, code, sc = datagen.random_entries(C, 5151, scale_range=(1e-3, 10.0))
+    code = code.copy()
+    code[3] = 1                     # a crafted chunk: every entry at the +s level
+    code[4] = 3                     # every entry at -s
+    sc = sc.copy()
+    sc[[5, 6]] = [0.0, -0.0]        # empty chunks, well-formed
+    sc[7] = np.nan                  # flagged: non-finite
+    sc[8] = -2.0                    # flagged: negative
+    sc[9] = np.inf                  # flagged: non-finite, above every finite scale
+    idx = idx.copy()
+    idx[10, [2, 3]] = idx[10, [3, 2]]   # flagged: order; its scale still counts
+    sc[10] = 1e30
+    payload = orc.pack(idx, code)
+    counts, top = orc.peer_stats(payload, sc)
+
+    bad = {7, 8, 9, 10}
+    mag = int((code & 1).astype(bool).sum())
+    neg = int((code & 2).astype(bool).sum())
+    bit_mag = bit_neg = 0
+    for c in range(C):
+        _, cd = unpack_payload_bitwise(payload[c])
+        bit_mag += int((cd & 1).sum())
+        bit_neg += int((cd >> 1).sum())
+    assert (mag, neg) == (bit_mag, bit_neg)
+    valid = np.isfinite(sc) & ~(sc < 0)
+    assert counts.tolist() == [len(bad), 2, mag, neg]
+    assert bits(top) == bits(np.max(np.where(valid, sc, 0.0)).astype(np.float32))
+    assert top == np.float32(1e30)   # a record flagged only for its order keeps its scale in the maximum
+
+
+def test_peer_stats_edge_cases(orc):
+    """No records; only invalid scales (the maximum stays +0); -0 alone gives
+    +0, not -0."""
+    counts, top = orc.peer_stats(np.zeros((0, 112), np.uint8), np.zeros(0, np.float32))
+    assert counts.tolist() == [0, 0, 0, 0] and bits(top) == 0
+    idx, code, sc = datagen.random_entries(3, 8, scale_range=(1.0, 2.0))
+    payload = orc.pack(idx, code)
+    counts, top = orc.peer_stats(payload, np.float32([np.nan, -1.0, -np.inf]))
+    assert counts[0] == 3 and bits(top) == 0
+    counts, top = orc.peer_stats(payload, np.float32([-0.0, -0.0, -0.0]))
+    assert counts[:2].tolist() == [0, 3] and bits(top) == 0

@@ -7,7 +7,7 @@ shows the pins are tied to the pages and to mathematics, not to the oracle's own
 code.  Mistakes are chosen where a reading of the pages could plausibly go
 wrong: tie rule, threshold strictness, rounding of s/3 and of the error-feedback
 update, entry order, code-bit and bit-stream layout, sign of zero, the scale,
-the residual, the peer order, the outer update and the validator.
+the residual, the peer order, the outer update, the validator and the per-peer statistics.
 """
 import os
 import subprocess
@@ -59,6 +59,13 @@ MUTANTS = [
      [("theta[i] - out[i] / denom;", "theta[i] - out[i] * (1.0f / denom);")]),
     ("validator accepts repeated indices",
      [("if (!(idx[j] > idx[j - 1])) f |= 1;", "if (!(idx[j] >= idx[j - 1])) f |= 1;")]),
+    ("statistics count the sign bit as magnitude",
+     [("if (code[j] & 1u) ++magnitude;", "if (code[j] & 2u) ++magnitude;")]),
+    ("statistics take the maximum over every scale",
+     [("if ((f & 6u) == 0 && s > top) top = s;", "if (s > top) top = s;")]),
+    ("statistics skip the code counts of flagged records",
+     [("        unpack_one(payload + c * kPayloadBytes, idx, code);\n        for (int32_t j = 0; j < kTopK; ++j) {",
+       "        unpack_one(payload + c * kPayloadBytes, idx, code);\n        if (f) continue;\n        for (int32_t j = 0; j < kTopK; ++j) {")]),
     ("pseudo-gradient sign flipped",
      [("delta[i] = theta_pre[i] - theta_post[i];", "delta[i] = theta_post[i] - theta_pre[i];")]),
 ]
