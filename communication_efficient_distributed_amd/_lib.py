@@ -29,8 +29,8 @@ STATUS = {
 }
 
 EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_apply",
-           "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_host_device_pointer",
-           "sl_status_string")
+           "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_peer_stats",
+           "sl_host_device_pointer", "sl_status_string")
 
 
 class SparseLoCoError(RuntimeError):
@@ -65,6 +65,8 @@ def load():
     L.sl_validate_payload.restype = ctypes.c_int
     L.sl_validate_payloads.argtypes = [P, P, I32, I64, P, P]
     L.sl_validate_payloads.restype = ctypes.c_int
+    L.sl_peer_stats.argtypes = [P, P, I32, I64, P, P, P, P]
+    L.sl_peer_stats.restype = ctypes.c_int
     L.sl_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
     L.sl_host_device_pointer.restype = ctypes.c_int
     L.sl_aggregate.argtypes = [P, P, I32, P, I64, P]
@@ -199,11 +201,42 @@ def sl_validate_payloads(payloads, scales, flags: torch.Tensor, stream=None) -> 
                                                                    _stream_of(flags, stream)))
 
 
+def sl_peer_stats(payloads, scales, counts: torch.Tensor, scale_max: torch.Tensor, flags=None,
+                  n_chunks: int | None = None, stream=None) -> None:
+    """Per-peer statistics of the received records, one pass.  counts is int64
+    [n_peers, 4]: records flagged by validation, records with scale +-0,
+    entries at the magnitude level, entries with the sign bit; scale_max is
+    float32 [n_peers], the largest finite non-negative scale.  flags, if given,
+    is uint8 [n_peers, n_chunks] and receives the validation flags.  n_chunks
+    defaults to the peers' record count (peer 0's, or the PeerSet's)."""
+    N = len(payloads)
+    if counts.dim() != 2 or tuple(counts.shape) != (N, 4):
+        raise ValueError("counts must be a [n_peers, 4] tensor")
+    if scale_max.numel() != N:
+        raise ValueError("scale_max must hold n_peers floats")
+    if n_chunks is None:
+        if flags is not None:
+            n_chunks = flags.shape[1] if flags.dim() == 2 else -1
+        elif isinstance(payloads, PeerSet):
+            n_chunks = payloads.n_chunks
+        else:
+            n_chunks = scales[0].numel() if N else 0
+    if flags is not None and (flags.dim() != 2 or tuple(flags.shape) != (N, n_chunks)):
+        raise ValueError("flags must be a [n_peers, n_chunks] tensor")
+    N, pa, sa, _keep = _peer_arrays(payloads, scales, n_chunks)
+    c = _dev(counts, "counts", torch.int64)
+    m = _dev(scale_max, "scale_max", torch.float32)
+    f = _dev(flags, "flags", torch.uint8) if flags is not None else ctypes.c_void_p(None)
+    with torch.cuda.device(counts.device):
+        _check("sl_peer_stats", load().sl_peer_stats(pa, sa, ctypes.c_int32(N), ctypes.c_int64(n_chunks), f, c, m,
+                                                     _stream_of(counts, stream)))
+
+
 class PeerSet:
     """The peers' record and scale tensors, checked once, with the C pointer
     tables kept for repeated calls (receive buffers reused round after round).
     Pass it as `payloads` (with `scales=None`) to sl_aggregate,
-    sl_aggregate_apply, aggregate and sl_validate_payloads.  The tensors are
+    sl_aggregate_apply, aggregate, sl_validate_payloads and sl_peer_stats.  The tensors are
     held, so their storage stays alive; their contents may change between
     calls, their storage must not be replaced."""
 

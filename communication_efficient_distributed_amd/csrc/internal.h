@@ -28,6 +28,12 @@ hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float
 hipError_t launch_validate(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
                            hipStream_t stream);
 
+// Per-peer statistics (and, if flags is not null, the validation flags) of
+// n_peers peers' n_chunks records.  counts: int64[n_peers][4], scale_max:
+// float32[n_peers]; both are cleared by the first of the two kernels.
+hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
+                             int64_t* counts, float* scale_max, hipStream_t stream);
+
 hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
                                    float beta, uint8_t* payload, float* scales, int64_t n_chunks,
                                    hipStream_t stream);

@@ -116,6 +116,40 @@ sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* cons
     return from_hip(sl::launch_validate(table, n_peers, n_chunks, flags, static_cast<hipStream_t>(stream)));
 }
 
+sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
+                        int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max, void* stream) {
+    if (n_chunks < 0 || n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n_peers == 0) return SL_OK;
+    if (!counts || !scale_max) return SL_ERR_INVALID_ARG;
+    if (!aligned(counts, 8) || !aligned(scale_max, 4)) return SL_ERR_ALIGN;
+    const size_t cbytes = (size_t)n_peers * 4 * sizeof(int64_t);
+    const size_t mbytes = (size_t)n_peers * sizeof(float);
+    const size_t fbytes = flags ? (size_t)n_peers * (size_t)n_chunks : 0;
+    if (overlap(counts, cbytes, scale_max, mbytes) || overlap(flags, fbytes, counts, cbytes) ||
+        overlap(flags, fbytes, scale_max, mbytes))
+        return SL_ERR_INVALID_ARG;
+    sl::PeerTable table = {};
+    if (n_chunks > 0) {
+        if (!payloads || !scales) return SL_ERR_INVALID_ARG;
+        const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+        const size_t sbytes = (size_t)n_chunks * sizeof(float);
+        for (int32_t p = 0; p < n_peers; ++p) {
+            if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
+            if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
+            const void* bufs[3] = {flags, counts, scale_max};
+            const size_t lens[3] = {fbytes, cbytes, mbytes};
+            for (int b = 0; b < 3; ++b)
+                if (overlap(bufs[b], lens[b], payloads[p], pbytes) || overlap(bufs[b], lens[b], scales[p], sbytes))
+                    return SL_ERR_INVALID_ARG;
+            table.payload[p] = payloads[p];
+            table.scales[p] = scales[p];
+        }
+    }
+    return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 namespace {

@@ -209,6 +209,34 @@ sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* cons
                                int32_t n_peers, int64_t n_chunks, uint8_t* flags, void* stream);
 
 /*
+ * sl_peer_stats -- per-peer statistics of a round's received records, with
+ * the validation flags of sl_validate_payloads in the same pass.
+ *
+ * [SF] "What the Blockchain Does (and Doesn't Do)": the defence against
+ * poisoned updates was that a crafted sparse update looks different to anomaly
+ * detection.  Reading: the statistics such screening starts from, exact and
+ * independent of the launch, for each peer p over its n_chunks records:
+ *   counts[4p + 0]  records with any validation flag set
+ *   counts[4p + 1]  records whose scale is +0 or -0 (empty chunks)
+ *   counts[4p + 2]  entries at the magnitude level, code bit 0 (all records)
+ *   counts[4p + 3]  entries with the sign bit, code bit 1 (all records)
+ *   scale_max[p]    the largest scale among records whose scale is finite and
+ *                   not negative (-0 counts as +0); +0 if there is none
+ *
+ * payloads, scales  as for sl_validate_payloads
+ * n_peers   0..SL_MAX_PEERS (0 is a no-op), else SL_ERR_TOO_MANY_PEERS
+ * n_chunks  records per peer; with 0 the statistics are all written as 0
+ * flags     out uint8[n_peers][n_chunks] as for sl_validate_payloads, or NULL
+ *           to skip them
+ * counts    out int64[n_peers][4] (device, 8-byte aligned), overwritten
+ * scale_max out float32[n_peers] (device, 4-byte aligned), overwritten
+ * No output may overlap another output or any payload or scale buffer.
+ */
+sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
+                        int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
+                        void* stream);
+
+/*
  * sl_host_device_pointer -- device address of pinned, mapped host memory.
  *
  * Error-feedback offload ([CV] "SparseLoCo: Breaking the Bandwidth Barrier":

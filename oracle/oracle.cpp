@@ -38,7 +38,7 @@
  *   R8 ef <- acc - decoded at kept positions, acc elsewhere.
  *   R9 aggregation returns the sum, from +0.0, peers in ascending order.
  *   R10 outer update theta <- theta - sum / N (correctly rounded division).
- *   R11 per-peer statistics for anomaly screening ([SF], "What the Blockchain
+ *   R13 per-peer statistics for anomaly screening ([SF], "What the Blockchain
  *       Does (and Doesn't Do)": a crafted sparse update stands out to anomaly
  *       detection): records flagged by the validator, records with a zero
  *       scale, entries at the magnitude level, entries with the sign bit, and
@@ -292,7 +292,7 @@ int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chun
 
 void orc_peer_stats(const uint8_t* payload, const float* scales, int64_t n_chunks,
                     int64_t* counts, float* scale_max) {
-    /* R11.  Flags as in orc_validate; the code counts take every record as
+    /* R13.  Flags as in orc_validate; the code counts take every record as
      * received, well-formed or not. */
     int64_t bad = 0, zero_scale = 0, magnitude = 0, negative = 0;
     float top = 0.0f;

@@ -75,7 +75,7 @@ int orc_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n);
 int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chunks,
                      uint8_t* bad);
 
-/* Statistics of one peer's n_chunks received records (reading R11):
+/* Statistics of one peer's n_chunks received records (reading R13):
  * counts[0] records that orc_validate flags, counts[1] records whose scale is
  * +0 or -0, counts[2] entries with code bit 0 (magnitude level), counts[3]
  * entries with code bit 1 (sign); *scale_max = the largest scale among records

@@ -37,8 +37,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_apply",
-              "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_host_device_pointer",
-              "sl_status_string"):
+              "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_peer_stats",
+              "sl_host_device_pointer", "sl_status_string"):
         assert n in names
 
 
@@ -239,6 +239,42 @@ def test_validate_many_argument_checks(lib):
     assert call(pp, ss, 3, flags=pp[1] + 16) == SL_ERR_INVALID_ARG      # flags overlap a record
     assert call(pp, ss, 3, flags=ss[2] - 8) == SL_ERR_INVALID_ARG       # flags (48 bytes) reach a scale buffer
     assert lib.sl_validate_payloads(None, None, 2, 16, F, None) == SL_ERR_INVALID_ARG
+
+
+def test_peer_stats_argument_checks(lib):
+    """Every call here is rejected (or is a no-op) on the host, before any
+    launch."""
+    F = A * 1200
+    CNT = A * 1300
+    MX = A * 1400
+    pp = [P + k * A for k in range(3)]
+    ss = [S + k * A for k in range(3)]
+
+    def call(peers, scales, n_peers, n_chunks=16, flags=F, counts=CNT, smax=MX):
+        pa = (ctypes.c_void_p * max(len(peers), 1))(*peers)
+        sa = (ctypes.c_void_p * max(len(scales), 1))(*scales)
+        return lib.sl_peer_stats(ctypes.cast(pa, ctypes.c_void_p), ctypes.cast(sa, ctypes.c_void_p),
+                                 n_peers, n_chunks, flags, counts, smax, None)
+
+    assert call(pp, ss, 3, n_chunks=-1) == SL_ERR_SHAPE
+    assert call(pp, ss, 3, n_chunks=1 << 31) == SL_ERR_SHAPE
+    assert call(pp, ss, -1) == SL_ERR_TOO_MANY_PEERS
+    assert call(pp, ss, 129) == SL_ERR_TOO_MANY_PEERS
+    assert call(pp, ss, 0) == SL_OK                                     # no-op
+    assert call(pp, ss, 3, counts=None) == SL_ERR_INVALID_ARG
+    assert call(pp, ss, 3, smax=None) == SL_ERR_INVALID_ARG
+    assert call(pp, ss, 3, counts=CNT + 4) == SL_ERR_ALIGN
+    assert call(pp, ss, 3, smax=MX + 2) == SL_ERR_ALIGN
+    assert call([pp[0], None, pp[2]], ss, 3) == SL_ERR_INVALID_ARG
+    assert call(pp, [ss[0], None, ss[2]], 3) == SL_ERR_INVALID_ARG
+    assert call([pp[0], pp[1] + 8, pp[2]], ss, 3) == SL_ERR_ALIGN
+    assert call(pp, [ss[0], ss[1] + 2, ss[2]], 3) == SL_ERR_ALIGN
+    assert call(pp, ss, 3, counts=MX - 8) == SL_ERR_INVALID_ARG         # counts (96 bytes) reach scale_max
+    assert call(pp, ss, 3, flags=CNT - 8) == SL_ERR_INVALID_ARG         # flags (48 bytes) reach counts
+    assert call(pp, ss, 3, counts=pp[1] + 16) == SL_ERR_INVALID_ARG     # counts inside a record buffer
+    assert call(pp, ss, 3, smax=ss[2]) == SL_ERR_INVALID_ARG            # scale_max on a scale buffer
+    assert call(pp, ss, 3, flags=pp[0]) == SL_ERR_INVALID_ARG           # flags on a record buffer
+    assert lib.sl_peer_stats(None, None, 2, 16, None, CNT, MX, None) == SL_ERR_INVALID_ARG
 
 
 def test_peerset_checks_once_and_rejects_bad_tensors():

@@ -74,15 +74,12 @@ def test_validate_payload_flags(orc):
     assert_bitwise(flags.cpu().numpy(), want, "flags")
 
 
-def test_validate_many_peers_in_one_launch(orc):
-    """sl_validate_payloads over 24 peers and a ragged 1000 records each, with
-    defects planted in some peers (order, duplicates, NaN of either sign, -inf,
-    negative and negative-denormal scales, -0 which is allowed), row by row
-    against the oracle."""
-    sl = require_gpu()
-    N, C = 24, 1000
-    rng = np.random.default_rng(17)
-    payloads, scales, want = [], [], []
+def defective_peers(orc, N, C, seed):
+    """N peers of C records each; every third peer gets 40 defects (order,
+    duplicates, NaN of either sign, -inf, negative denormal scale, -0 which is
+    allowed, reversed indices)."""
+    rng = np.random.default_rng(seed)
+    payloads, scales = [], []
     for p in range(N):
         idx, code, sc = datagen.random_entries_bulk(C, 900 + p)
         if p % 3 == 1:
@@ -107,11 +104,25 @@ def test_validate_many_peers_in_one_launch(orc):
                     sc[c] = -0.0                                      # allowed
                 else:
                     idx[c] = idx[c][::-1]
-        pl = orc.pack(idx, code)
-        payloads.append(pl)
+        if p % 4 == 2:
+            code[rng.choice(C, 9, replace=False)] = 1                 # crafted: all entries at +s
+            sc[rng.choice(C, 5, replace=False)] = 0.0                 # empty chunks
+        if p == 5:
+            sc[3] = np.inf                                            # flagged, above every finite scale
+            sc[4] = np.float32(3e38)                                  # the largest valid scale
+        payloads.append(orc.pack(idx, code))
         scales.append(sc)
-        want.append(orc.validate(pl, sc)[1])
-    assert sum(int((w != 0).sum()) for w in want) == 8 * 35
+    return payloads, scales
+
+
+def test_validate_many_peers_in_one_launch(orc):
+    """sl_validate_payloads over 24 peers and a ragged 1000 records each, with
+    defects planted in some peers, row by row against the oracle."""
+    sl = require_gpu()
+    N, C = 24, 1000
+    payloads, scales = defective_peers(orc, N, C, 17)
+    want = [orc.validate(pl, sc)[1] for pl, sc in zip(payloads, scales)]
+    assert sum(int((w != 0).sum()) for w in want) >= 8 * 34      # defects planted (a few may be overwritten)
     flags = torch.full((N, C), 255, dtype=torch.uint8, device="cuda")
     note("sl_validate_payloads 24 peers x 1000 records")
     sl.sl_validate_payloads([torch.from_numpy(x).cuda() for x in payloads],
@@ -120,6 +131,66 @@ def test_validate_many_peers_in_one_launch(orc):
     got = flags.cpu().numpy()
     for p in range(N):
         assert_bitwise(got[p], want[p], f"flags of peer {p}")
+
+
+def check_peer_stats(sl, orc, payloads, scales, with_flags=True):
+    N, C = len(payloads), scales[0].size
+    counts = torch.full((N, 4), -1, dtype=torch.int64, device="cuda")
+    smax = torch.full((N,), -1.0, dtype=torch.float32, device="cuda")
+    flags = torch.full((N, C), 255, dtype=torch.uint8, device="cuda") if with_flags else None
+    peers = sl.PeerSet([torch.from_numpy(x).cuda() for x in payloads], [torch.from_numpy(x).cuda() for x in scales])
+    note(f"sl_peer_stats {N} peers x {C} records, flags={with_flags}")
+    sl.sl_peer_stats(peers, None, counts, smax, flags=flags)
+    torch.cuda.synchronize()
+    got_c, got_m = counts.cpu().numpy(), smax.cpu().numpy()
+    for p in range(N):
+        wc, wm = orc.peer_stats(payloads[p], scales[p])
+        assert got_c[p].tolist() == wc.tolist(), f"counts of peer {p}"
+        assert_bitwise(got_m[p:p + 1], np.float32([wm]), f"scale_max of peer {p}")
+    if with_flags:
+        got_f = flags.cpu().numpy()
+        for p in range(N):
+            assert_bitwise(got_f[p], orc.validate(payloads[p], scales[p])[1], f"flags of peer {p}")
+    return got_c, got_m
+
+
+def test_peer_stats_against_the_oracle(orc):
+    """sl_peer_stats over 24 peers x 1000 records with planted defects,
+    crafted all-magnitude chunks, zero scales and an infinite scale; counts,
+    maxima and flags against the oracle; without flags the statistics are the
+    same."""
+    sl = require_gpu()
+    payloads, scales = defective_peers(orc, 24, 1000, 17)
+    a = check_peer_stats(sl, orc, payloads, scales, with_flags=True)
+    b = check_peer_stats(sl, orc, payloads, scales, with_flags=False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert a[1][5] == np.float32(3e38)
+
+
+@pytest.mark.parametrize("N,C", [(1, 1), (3, 63), (128, 257), (24, 57344)])
+def test_peer_stats_shapes(orc, N, C):
+    """One record, ragged counts, the most peers, and the full 8192 x 28672
+    shape with 24 peers."""
+    sl = require_gpu()
+    payloads, scales = [], []
+    for p in range(N):
+        idx, code, sc = datagen.random_entries_bulk(C, 3100 + p)
+        payloads.append(orc.pack(idx, code))
+        scales.append(sc)
+    check_peer_stats(sl, orc, payloads, scales, with_flags=(N * C <= 200000))
+
+
+def test_peer_stats_without_records():
+    """n_chunks = 0: the statistics are still written, all zero."""
+    sl = require_gpu()
+    counts = torch.full((3, 4), 7, dtype=torch.int64, device="cuda")
+    smax = torch.full((3,), 7.0, dtype=torch.float32, device="cuda")
+    e = [torch.empty(0, dtype=torch.uint8, device="cuda")] * 3
+    s = [torch.empty(0, dtype=torch.float32, device="cuda")] * 3
+    note("sl_peer_stats n_chunks=0")
+    sl.sl_peer_stats(e, s, counts, smax)
+    torch.cuda.synchronize()
+    assert not counts.any() and smax.view(torch.int32).eq(0).all()
 
 
 def test_compressor_output_is_well_formed():
