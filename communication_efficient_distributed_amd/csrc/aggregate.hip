@@ -232,8 +232,10 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
 }
 
 // theta <- theta - out / n_peers.  One workgroup of four wavefronts per
-// 4096-element chunk, four float4 of each stream per lane, nontemporal loads
-// and stores.
+// 4096-element chunk; wavefront w streams its own contiguous quarter (four
+// float4 of each stream per lane, 1 KiB per instruction), nontemporal loads
+// and stores.  (Interleaving the four wavefronts at 1 KiB within each 4 KiB
+// measured 3% slower: 443-446 us against 430-431 us at 8192 x 28672.)
 constexpr int kMeanWaves = 4;
 constexpr int kMeanSlots = SL_CHUNK / (4 * kWave * kMeanWaves);  // 4
 
@@ -242,17 +244,18 @@ __global__ __launch_bounds__(kWave * kMeanWaves) void apply_mean_kernel(float* t
     const int tid = (int)threadIdx.x;
     const int64_t chunk = (int64_t)blockIdx.x;
     if (chunk >= n_chunks) return;
-    const size_t base = (size_t)chunk * SL_CHUNK + 4 * (size_t)tid;
+    const size_t base = (size_t)chunk * SL_CHUNK + (size_t)(SL_CHUNK / kMeanWaves) * (size_t)(tid >> 6) +
+                        4 * (size_t)(tid & (kWave - 1));
     v4f t[kMeanSlots], o[kMeanSlots];
 #pragma unroll
     for (int m = 0; m < kMeanSlots; ++m) {
-        const size_t off = base + (size_t)(4 * kWave * kMeanWaves) * m;
+        const size_t off = base + (size_t)(4 * kWave) * m;
         t[m] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(theta + off));
         o[m] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(out + off));
     }
 #pragma unroll
     for (int m = 0; m < kMeanSlots; ++m) {
-        const size_t off = base + (size_t)(4 * kWave * kMeanWaves) * m;
+        const size_t off = base + (size_t)(4 * kWave) * m;
         v4f r;
         r.x = t[m].x - o[m].x / nf;
         r.y = t[m].y - o[m].y / nf;
@@ -263,8 +266,8 @@ __global__ __launch_bounds__(kWave * kMeanWaves) void apply_mean_kernel(float* t
 }
 
 // Residency cap of apply_mean (workgroups per CU, through unused dynamic
-// LDS).  On 8192 x 28672 parameters: 437-443 us at 2 or 3, 454-457 us at 4,
-// 463-466 us for the earlier one-wavefront-per-chunk kernel.  The aggregator
+// LDS).  On 8192 x 28672 parameters: 429-431 us at 2 or 3, 441-442 us at 4;
+// the earlier one-wavefront-per-chunk kernel ran 463-466 us.  The aggregator
 // is left uncapped (9 workgroups per CU by its own LDS): capping it at 8 gained
 // 1%, at 6 or 4 it lost 11% and 52%.
 constexpr int kCapApplyMean = 3;
