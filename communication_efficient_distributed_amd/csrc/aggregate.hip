@@ -20,6 +20,9 @@
 //      deterministic, no atomics;
 //   3. the tile is streamed to HBM with 16-byte stores (or, fused, theta is
 //      updated in place).
+// The fused update for up to 27 peers uses four wavefronts per chunk instead:
+// wavefront 0 runs steps 1-2 while each wavefront loads its own quarter of
+// theta, then each updates its quarter from the tile.
 //
 // Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
@@ -137,29 +140,16 @@ __device__ __forceinline__ void load_theta(const float* theta_chunk, v4f (&th)[k
     }
 }
 
-// Up to 9 * NGMAX peers, one chunk per workgroup (one wavefront).  Every record
-// slice of the chunk is loaded into registers up front (NGMAX loads of 16 bytes
-// per lane, 9 peers each; lanes past the last peer re-read peer 0, so no load
-// sits in a divergent branch).  The tile keeps the partial sums while the peers
-// are staged 9 at a time in a separate 1.1 KiB area: 17.1 KiB of LDS per
-// workgroup leaves room for 9 of them per CU.  dst is the dense update (0 peers
-// allowed) or, with APPLY, theta (n_peers >= 1).
-template <int NGMAX, bool APPLY>
-__global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32_t n_peers, float* dst,
-                                                          int64_t n_chunks, int64_t per_xcd, float nf) {
+// The sums of chunk `chunk` over up to 9 * NGMAX peers, into the LDS tile
+// (cleared here), in ascending peer order; run by one wavefront.  Every record
+// slice of the chunk is loaded into registers up front (NGMAX loads of 16
+// bytes per lane, 9 peers each; lanes past the last peer re-read peer 0, so no
+// load sits in a divergent branch); `issued()` runs once the loads are in
+// flight.  The peers are then staged 9 at a time in `stage` (1.1 KiB).
+template <int NGMAX, typename Issued>
+__device__ __forceinline__ void sum_chunk(const PeerTable& peers, int32_t n_peers, int64_t chunk, float* tile,
+                                          uint32_t* stage, int lane, Issued issued) {
     constexpr int kMaxPeers = kPeersPerLoad * NGMAX;
-    __shared__ __align__(16) float tile[SL_CHUNK];
-    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
-    const int lane = (int)threadIdx.x;
-    const int64_t chunk = xcd_chunk(per_xcd);
-    if (chunk >= n_chunks) return;
-    float* dst_chunk = dst + (size_t)chunk * SL_CHUNK;
-    if (!APPLY && n_peers == 0) {  // the empty sum; the peer table is empty
-        clear_tile(tile, lane);
-        wave_sync();
-        store_tile(tile, dst_chunk, lane);
-        return;
-    }
     const int rp = lane / kQuads;
     const int rq = lane - kQuads * rp;
     const EntryPos pos(lane);
@@ -201,10 +191,7 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
 #pragma unroll
         for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(r[g]));
     }
-    // theta is loaded early unless the records already hold most registers.
-    constexpr bool kEarlyTheta = NGMAX <= 9;
-    v4f th[kSlots];
-    if constexpr (kEarlyTheta) load_theta<APPLY>(dst_chunk, th, lane);
+    issued();
 
     const int slot = rp < kPeersPerLoad ? rp : kPeersPerLoad;  // lane 63: dummy slot 9
     clear_tile(tile, lane);
@@ -226,9 +213,82 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
                               __uint_as_float(read_lane(__float_as_uint(s3v), q)));
         }
     }
+}
+
+// One chunk per workgroup of one wavefront.  The tile keeps the partial sums:
+// 17.1 KiB of LDS per workgroup leaves room for 9 of them per CU.  dst is the
+// dense update (0 peers allowed) or, with APPLY, theta (n_peers >= 1).
+template <int NGMAX, bool APPLY>
+__global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32_t n_peers, float* dst,
+                                                          int64_t n_chunks, int64_t per_xcd, float nf) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = xcd_chunk(per_xcd);
+    if (chunk >= n_chunks) return;
+    float* dst_chunk = dst + (size_t)chunk * SL_CHUNK;
+    if (!APPLY && n_peers == 0) {  // the empty sum; the peer table is empty
+        clear_tile(tile, lane);
+        wave_sync();
+        store_tile(tile, dst_chunk, lane);
+        return;
+    }
+    // theta is loaded early unless the records already hold most registers.
+    constexpr bool kEarlyTheta = NGMAX <= 9;
+    v4f th[kSlots];
+    sum_chunk<NGMAX>(peers, n_peers, chunk, tile, stage, lane, [&] {
+        if constexpr (kEarlyTheta) load_theta<APPLY>(dst_chunk, th, lane);
+    });
     if constexpr (!kEarlyTheta) load_theta<APPLY>(dst_chunk, th, lane);
     wave_sync();
     finish_chunk<APPLY>(tile, dst_chunk, th, nf, lane);
+}
+
+// Fused outer update with four wavefronts per chunk: wavefront 0 sums the
+// peers into the tile as above, while every wavefront w loads its own
+// contiguous quarter of theta (slots 4w..4w+3, four float4 per lane); after
+// one barrier each updates and stores its quarter.  Same fp32 operations per
+// element as aggregate_kernel<NGMAX, true>.
+constexpr int kApplyWaves = 4;
+constexpr int kQuarterSlots = kSlots / kApplyWaves;
+
+template <int NGMAX>
+__global__ __launch_bounds__(kWave * kApplyWaves) void aggregate_apply4_kernel(PeerTable peers, int32_t n_peers,
+                                                                               float* theta, int64_t n_chunks,
+                                                                               int64_t per_xcd, float nf) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t chunk = xcd_chunk(per_xcd);
+    if (chunk >= n_chunks) return;  // the whole workgroup
+    float* th_chunk = theta + (size_t)chunk * SL_CHUNK;
+    v4f th[kQuarterSlots];
+    auto load_quarter = [&] {
+#pragma unroll
+        for (int m = 0; m < kQuarterSlots; ++m)
+            th[m] = __builtin_nontemporal_load(
+                reinterpret_cast<const v4f*>(th_chunk + 4 * ((kQuarterSlots * w + m) * kWave + lane)));
+    };
+    if (w == 0)
+        sum_chunk<NGMAX>(peers, n_peers, chunk, tile, stage, lane, load_quarter);
+    else
+        load_quarter();
+    __syncthreads();
+    const float4* t4 = reinterpret_cast<const float4*>(tile);
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(th_chunk);
+#pragma unroll
+    for (int m = 0; m < kQuarterSlots; ++m) {
+        const int slot = kQuarterSlots * w + m;
+        const float4 o = t4[slot * kWave + lane];
+        v4f r;
+        r.x = th[m].x - o.x / nf;
+        r.y = th[m].y - o.y / nf;
+        r.z = th[m].z - o.z / nf;
+        r.w = th[m].w - o.w / nf;
+        store_slot<kStorePolicy>(rs, slot, lane, r);
+    }
 }
 
 // theta <- theta - out / n_peers.  One workgroup of four wavefronts per
@@ -289,7 +349,26 @@ hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float*
                     : n_peers <= kPeersPerLoad * 6 ? reinterpret_cast<const void*>(&aggregate_kernel<6, APPLY>)
                     : n_peers <= kPeersPerLoad * 9 ? reinterpret_cast<const void*>(&aggregate_kernel<9, APPLY>)
                                                    : reinterpret_cast<const void*>(&aggregate_kernel<15, APPLY>);
-    return hipLaunchKernel(k, dim3((unsigned)(per_xcd * kXcds)), dim3(kWave), args, 0, stream);
+    const dim3 grid((unsigned)(per_xcd * kXcds));
+    // The fused update for up to 27 peers runs four wavefronts per chunk,
+    // with a residency cap that depends on the chain length.  At 8192 x 28672
+    // (one wavefront per chunk: 312-316 us for 1-27 peers) it took 294-298 us
+    // for 1-18 peers at 5 workgroups per CU (cap 7: 308 us), and 308-311 us
+    // for 24-27 peers at 7 (cap 5: 314-319 us; uncapped 310-312 us).
+    // Beyond 27 peers the chain needs the one-wavefront kernel's 9 chunks in
+    // flight per CU.
+    if constexpr (APPLY) {
+        if (n_peers <= kPeersPerLoad * 3) {
+            constexpr size_t kStatic = sizeof(float) * SL_CHUNK + sizeof(uint32_t) * (kPeersPerLoad + 1) * kRecWords;
+            static_assert(cap_is_exact(5, kStatic) && cap_is_exact(7, kStatic), "residency caps");
+            const void* k4 = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_apply4_kernel<1>)
+                             : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_apply4_kernel<2>)
+                                                            : reinterpret_cast<const void*>(&aggregate_apply4_kernel<3>);
+            const int cap = n_peers <= kPeersPerLoad * 2 ? 5 : 7;
+            return hipLaunchKernel(k4, grid, dim3(kWave * kApplyWaves), args, residency_lds(cap, kStatic), stream);
+        }
+    }
+    return hipLaunchKernel(k, grid, dim3(kWave), args, 0, stream);
 }
 
 }  // namespace

@@ -179,7 +179,7 @@ def test_mlp_8192x28672_full(orc):
     assert_bitwise(g, o, "mlp aggregate")
 
 
-@pytest.mark.parametrize("n_peers", [1, 9, 10, 24, 28, 64, 81, 128])
+@pytest.mark.parametrize("n_peers", [1, 9, 10, 18, 19, 24, 27, 28, 64, 81, 128])
 def test_aggregate_apply_fused(orc, n_peers):
     """sl_aggregate_apply equals the oracle's aggregate followed by apply_mean,
     and the GPU's own two-call path, bit for bit."""
