@@ -1,7 +1,8 @@
 """A whole round captured in a HIP graph, through the C ABI.
 
-The round is: validate each peer's records, then the fused aggregate + outer
-update of theta, then compress the next pseudo-gradient.  The library issues
+The round is: validate each peer's records, take the per-peer statistics of
+all of them in one pass, then the fused aggregate + outer update of theta,
+then compress the next pseudo-gradient.  The library issues
 no allocation and no memset, so the captured kernels replay exactly as
 launched.  Every replay runs with eager work (input resets, host copies)
 between replays, and is compared with the oracle.
@@ -38,6 +39,7 @@ def test_round_replayed_from_a_graph(orc):
 
     # What the round must produce.
     want_flags = [orc.validate(pl, s)[1] for pl, s in zip(peers_p, peers_s)]
+    want_stats = [orc.peer_stats(pl, s) for pl, s in zip(peers_p, peers_s)]
     want_theta = orc.apply_mean(theta0, orc.aggregate(peers_p, peers_s, n), N)
     want_payload, want_scales, want_ef = orc.compress(delta0, ef0, beta=0.95)
 
@@ -50,6 +52,8 @@ def test_round_replayed_from_a_graph(orc):
     payload = torch.empty((C, 112), dtype=torch.uint8, device=dev)
     scales = torch.empty(C, dtype=torch.float32, device=dev)
     flags = torch.empty((N, C), dtype=torch.uint8, device=dev)
+    counts = torch.empty((N, 4), dtype=torch.int64, device=dev)
+    smax = torch.empty(N, dtype=torch.float32, device=dev)
     src = {k: torch.from_numpy(v).to(dev) for k, v in
            (("theta", theta0), ("delta", delta0), ("ef", ef0))}
 
@@ -60,10 +64,13 @@ def test_round_replayed_from_a_graph(orc):
         payload.zero_()
         scales.zero_()
         flags.fill_(0xFF)
+        counts.fill_(-1)                       # the statistics pass must clear its outputs itself
+        smax.fill_(-1.0)
 
     def round_():
         for p in range(N):
             sl.sl_validate_payload(dp[p], ds[p], flags[p])
+        sl.sl_peer_stats(dp, ds, counts, smax)
         sl.sl_aggregate_apply(dp, ds, theta)
         sl.sl_compress(delta, ef, 0.95, payload, scales)
 
@@ -71,6 +78,8 @@ def test_round_replayed_from_a_graph(orc):
         torch.cuda.synchronize()
         for p in range(N):
             assert_bitwise(flags[p].cpu().numpy(), want_flags[p], f"{what}: flags of peer {p}")
+            assert counts[p].cpu().tolist() == want_stats[p][0].tolist(), f"{what}: counts of peer {p}"
+            assert_bitwise(smax[p:p + 1].cpu().numpy(), np.float32([want_stats[p][1]]), f"{what}: scale_max of peer {p}")
         assert_bitwise(theta.cpu().numpy(), want_theta, f"{what}: theta")
         assert_bitwise(payload.cpu().numpy(), want_payload, f"{what}: payload")
         assert_bitwise(scales.cpu().numpy(), want_scales, f"{what}: scales")
