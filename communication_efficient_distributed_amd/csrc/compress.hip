@@ -50,12 +50,20 @@ constexpr uint32_t kSignBit = 0x80000000u;
 
 static_assert(SL_TOPK == kWave, "one kept entry per lane");
 static_assert(SL_INDEX_BITS == 12 && SL_CODE_BITS == 2, "payload layout");
-static_assert(SL_TOPK * kWaves + 128 + 64 + 64 <= kLdsWords, "entry segments and packing scratch fit");
-
+// Every phase has LDS of its own, so a phase never waits for the previous
+// one's readers before writing: the common path (boundary bin of at most 64
+// entries) crosses five workgroup barriers.
 struct Shared {
-    uint32_t lds[kLdsWords];  // histograms, candidate list, index bitmap, entries
-    uint32_t part[kWaves];    // one count or maximum per wavefront
-    uint32_t cut[3];          // the cut, broadcast by wavefront 0
+    uint32_t hist[kLdsWords];        // level-0 histogram; refinement histograms reuse it
+    uint32_t cand[SL_TOPK * kWaves]; // candidates, wavefront w's at [64 w, 64 w + 64); or the index bitmap
+    uint32_t ent[SL_TOPK * kWaves];  // kept entries, same segments
+    uint32_t bmp[SL_CHUNK / 32];     // packing: index bitmap
+    uint32_t pre[SL_TOPK];           //          per-64-index prefix counts
+    uint32_t sorted[SL_TOPK];        //          entries in index order
+    uint32_t part_max[kWaves];       // per-wavefront maximum key
+    uint32_t part_cnt[kWaves];       // per-wavefront candidate count
+    uint32_t part_sel[kWaves];       // per-wavefront kept-entry count
+    uint32_t cut[3];                 // the cut, broadcast by wavefront 0
 };
 
 __device__ __forceinline__ uint32_t key_of(float v) { return __float_as_uint(v) & kKeyMask; }
@@ -152,35 +160,45 @@ __device__ __forceinline__ void refine_histogram(const float (&acc)[kPerLane], u
     }
 }
 
+// Entry j (0..63) of the concatenation of the four wavefronts' segments, with
+// count[v] entries in segment v: segment and offset.
+__device__ __forceinline__ uint32_t segment_slot(const uint32_t* count, uint32_t j) {
+    uint32_t seg = 0, first = 0, start = 0;
+    for (int v = 0; v < kWaves; ++v) {
+        if (j >= start) {
+            seg = (uint32_t)v;
+            first = start;
+        }
+        start += count[v];
+    }
+    return SL_TOPK * seg + ((j - first) & (SL_TOPK - 1));
+}
+
 // At most 64 candidates (resolved bits == prefix) across the four wavefronts:
-// compact them into one LDS list (wavefront w after those of wavefronts < w),
-// rank them in wavefront 0 by (key descending, index ascending) and broadcast
-// the one at position need-1.  Candidates share the resolved bits, so (low
-// key bits, 4095 - index) fits one 32-bit sort word.
+// each wavefront compacts its own into its segment of sh.cand; wavefront 0
+// ranks them all by (key descending, index ascending) and broadcasts the one
+// at position need-1.  Candidates share the resolved bits, so (low key bits,
+// 4095 - index) fits one 32-bit sort word.
 __device__ __forceinline__ Cut rank_cut(const float (&acc)[kPerLane], Shared& sh, uint32_t pmask, uint32_t prefix,
                                         uint32_t lowmask, uint32_t need, uint32_t cnt, int w, int lane) {
+    uint32_t* seg = sh.cand + SL_TOPK * w;
     uint32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < kPerLane; ++q) mine += (uint32_t)__popcll(ballot((key_of(acc[q]) & pmask) == prefix));
-    if (lane == 0) sh.part[w] = mine;
-    __syncthreads();
-    uint32_t base = 0;
-    for (int v = 0; v < w; ++v) base += sh.part[v];
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         const uint32_t k = key_of(acc[q]);
         const bool c = (k & pmask) == prefix;
         const uint64_t bm = ballot(c);
         if (bm) {
-            const uint32_t pos = base + lanes_below(bm);
-            if (c && pos < (uint32_t)kWave) sh.lds[pos] = ((k & lowmask) << 12) | (4095u - elem_index(w, q, lane));
-            base += (uint32_t)__popcll(bm);
+            const uint32_t pos = mine + lanes_below(bm);
+            if (c && pos < (uint32_t)SL_TOPK) seg[pos] = ((k & lowmask) << 12) | (4095u - elem_index(w, q, lane));
+            mine += (uint32_t)__popcll(bm);
         }
     }
+    if (lane == 0) sh.part_cnt[w] = mine;
     __syncthreads();
     if (w == 0) {
         const bool mine_c = (uint32_t)lane < cnt;
-        const uint32_t sk = mine_c ? sh.lds[lane] : 0u;
+        const uint32_t sk = mine_c ? sh.cand[segment_slot(sh.part_cnt, (uint32_t)lane)] : 0u;
         uint32_t rank = 0;
         for (uint32_t f = 0; f < cnt; ++f) rank += read_lane(sk, (int)f) > sk ? 1u : 0u;
         const uint64_t hit = ballot(mine_c && rank == need - 1u);
@@ -200,18 +218,18 @@ __device__ __forceinline__ Cut rank_cut(const float (&acc)[kPerLane], Shared& sh
 // indices from all four wavefronts; wavefront 0 finds the need-th smallest.
 __device__ __forceinline__ Cut index_cut(const float (&acc)[kPerLane], Shared& sh, uint32_t K, uint32_t need,
                                          int w, int lane, int tid) {
-    if (tid < kWave) reinterpret_cast<uint2*>(sh.lds)[tid] = make_uint2(0u, 0u);
+    if (tid < kWave) reinterpret_cast<uint2*>(sh.cand)[tid] = make_uint2(0u, 0u);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         if (key_of(acc[q]) == K) {
             const uint32_t i = elem_index(w, q, lane);
-            block_lds_or(&sh.lds[i >> 5], 1u << (i & 31));
+            block_lds_or(&sh.cand[i >> 5], 1u << (i & 31));
         }
     }
     __syncthreads();
     if (w == 0) {
-        const uint2 wv = reinterpret_cast<const uint2*>(sh.lds)[lane];  // indices [64l, 64l+64)
+        const uint2 wv = reinterpret_cast<const uint2*>(sh.cand)[lane];  // indices [64l, 64l+64)
         const uint64_t wd = ((uint64_t)wv.y << 32) | wv.x;
         const uint32_t c = (uint32_t)__popcll(wd);
         const uint32_t incl = wave_prefix_sum(c, lane);
@@ -229,8 +247,8 @@ __device__ __forceinline__ Cut index_cut(const float (&acc)[kPerLane], Shared& s
     return broadcast_cut(sh);
 }
 
-// Every wavefront returns the same cut; every path ends with a workgroup
-// barrier, after which the LDS may be reused.
+// Every wavefront returns the same cut.  The level-0 histogram was cleared
+// before the barrier that published the wavefronts' maxima.
 __device__ __forceinline__ Cut select_cut(const float (&acc)[kPerLane], Shared& sh, uint32_t mx, int w, int lane,
                                           int tid) {
     Cut cut;
@@ -240,43 +258,40 @@ __device__ __forceinline__ Cut select_cut(const float (&acc)[kPerLane], Shared& 
         cut.key = 0u;
         cut.idx = 63u;
         cut.tie = true;
-        __syncthreads();
         return cut;
     }
     // Level 0: key bits 30..20.
-    clear_shared(sh.lds, kLdsWords, tid);
-    __syncthreads();
     uint32_t zeros = 0;
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
         const uint32_t k = key_of(acc[q]);
         const bool nz = k != 0u;
         zeros += (uint32_t)(kWave - __popcll(ballot(nz)));
-        if (nz) block_lds_add(&sh.lds[k >> 20], 1u);
+        if (nz) block_lds_add(&sh.hist[k >> 20], 1u);
     }
-    if (lane == 0 && zeros) block_lds_add(&sh.lds[0], zeros);
+    if (lane == 0 && zeros) block_lds_add(&sh.hist[0], zeros);
     __syncthreads();
-    Boundary b = find_boundary<kLdsWords / kWave>(sh.lds, (uint32_t)SL_TOPK, lane);
+    Boundary b = find_boundary<kLdsWords / kWave>(sh.hist, (uint32_t)SL_TOPK, lane);
     uint32_t need = (uint32_t)SL_TOPK - b.above;
     uint32_t prefix = b.digit << 20;
     uint32_t pmask = 0x7ff00000u;
-    __syncthreads();  // every wavefront has read the histogram
     if (b.count == need) {
         cut.key = prefix;
         return cut;
     }
     if (b.count <= (uint32_t)kWave) return rank_cut(acc, sh, pmask, prefix, 0x000fffffu, need, b.count, w, lane);
 
-    // Level 1: key bits 19..10 of the boundary bin.
-    clear_shared(sh.lds, 1024, tid);
+    // Level 1: key bits 19..10 of the boundary bin.  The histogram is reused
+    // once every wavefront has read it.
     __syncthreads();
-    refine_histogram<10>(acc, sh.lds, pmask, prefix, lane);
+    clear_shared(sh.hist, 1024, tid);
     __syncthreads();
-    b = find_boundary<1024 / kWave>(sh.lds, need, lane);
+    refine_histogram<10>(acc, sh.hist, pmask, prefix, lane);
+    __syncthreads();
+    b = find_boundary<1024 / kWave>(sh.hist, need, lane);
     need -= b.above;
     prefix |= b.digit << 10;
     pmask = 0x7ffffc00u;
-    __syncthreads();
     if (b.count == need) {
         cut.key = prefix;
         return cut;
@@ -284,15 +299,15 @@ __device__ __forceinline__ Cut select_cut(const float (&acc)[kPerLane], Shared& 
     if (b.count <= (uint32_t)kWave) return rank_cut(acc, sh, pmask, prefix, 0x3ffu, need, b.count, w, lane);
 
     // Level 2: key bits 9..0.
-    clear_shared(sh.lds, 1024, tid);
     __syncthreads();
-    refine_histogram<0>(acc, sh.lds, pmask, prefix, lane);
+    clear_shared(sh.hist, 1024, tid);
     __syncthreads();
-    b = find_boundary<1024 / kWave>(sh.lds, need, lane);
+    refine_histogram<0>(acc, sh.hist, pmask, prefix, lane);
+    __syncthreads();
+    b = find_boundary<1024 / kWave>(sh.hist, need, lane);
     need -= b.above;
     prefix |= b.digit;
     pmask = kKeyMask;
-    __syncthreads();
     if (b.count == need) {
         cut.key = prefix;
         return cut;
@@ -455,39 +470,25 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(const float* a, cons
         mx = k > mx ? k : mx;
     }
     mx = uniform(wave_max(mx));
-    if (lane == 0) sh.part[w] = mx;
+    clear_shared(sh.hist, kLdsWords, tid);
+    if (lane == 0) sh.part_max[w] = mx;
     __syncthreads();
-    for (int v = 0; v < kWaves; ++v) mx = sh.part[v] > mx ? sh.part[v] : mx;
-    __syncthreads();
+    for (int v = 0; v < kWaves; ++v) mx = sh.part_max[v] > mx ? sh.part_max[v] : mx;
 
     const Cut cut = select_cut(acc, sh, mx, w, lane, tid);
 
     const float s = __uint_as_float(mx);
     const float s3 = s / 3.0f;
     const uint32_t kmag = magnitude_threshold(s);
-    uint32_t* ent = sh.lds + SL_TOPK * w;  // this wavefront's kept entries
+    uint32_t* ent = sh.ent + SL_TOPK * w;  // this wavefront's kept entries
     const uint32_t nsel =
         cut.tie ? write_residual<true>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, w, lane)
                 : write_residual<false>(acc, cut, kmag, __float_as_uint(s), __float_as_uint(s3), ef + base, ent, w, lane);
-    if (lane == 0) sh.part[w] = nsel;
+    if (lane == 0) sh.part_sel[w] = nsel;
     __syncthreads();
     if (w == 0) {
-        // Entry j (0..63) of the chunk sits in the segment of the last
-        // wavefront whose entries start at or before j.
-        const uint32_t j = (uint32_t)lane;
-        uint32_t seg = 0, first = 0, start = 0;
-        for (int v = 0; v < kWaves; ++v) {
-            if (j >= start) {
-                seg = (uint32_t)v;
-                first = start;
-            }
-            start += sh.part[v];
-        }
-        const uint32_t e = sh.lds[SL_TOPK * seg + ((j - first) & (SL_TOPK - 1))];
-        uint32_t* bmp = sh.lds + SL_TOPK * kWaves;  // 128 words after the entry segments
-        uint32_t* pre = bmp + 128;                  // 64 words
-        uint32_t* sorted = pre + 64;                // 64 words
-        order_and_pack(e, bmp, pre, sorted, payload + (size_t)chunk * SL_PAYLOAD_BYTES, lane);
+        const uint32_t e = sh.ent[segment_slot(sh.part_sel, (uint32_t)lane)];
+        order_and_pack(e, sh.bmp, sh.pre, sh.sorted, payload + (size_t)chunk * SL_PAYLOAD_BYTES, lane);
         if (lane == 0) scales[chunk] = s;
     }
 }
