@@ -110,12 +110,12 @@ __device__ __forceinline__ Boundary find_boundary(const uint32_t* hist, uint32_t
         const uint4 v = h4[(r + rl) & (B / 4 - 1)];
         sum += v.x + v.y + v.z + v.w;
     }
-    const uint32_t S = wave_suffix_sum(sum, lane);
+    const uint32_t S = wave_suffix_sum(sum);
     int L = __popcll(ballot(S >= need)) - 1;
     L = L < 0 ? 0 : L;
     const uint32_t above_lane = read_lane(S, L) - read_lane(sum, L);
     const uint32_t h = lane < B ? hist[L * B + lane] : 0u;
-    const uint32_t T = wave_suffix_sum(h, lane);
+    const uint32_t T = wave_suffix_sum(h);
     int t = __popcll(ballot(lane < B && T + above_lane >= need)) - 1;
     t = t < 0 ? 0 : t;
     Boundary b;
@@ -232,7 +232,7 @@ __device__ __forceinline__ Cut index_cut(const float (&acc)[kPerLane], Shared& s
         const uint2 wv = reinterpret_cast<const uint2*>(sh.cand)[lane];  // indices [64l, 64l+64)
         const uint64_t wd = ((uint64_t)wv.y << 32) | wv.x;
         const uint32_t c = (uint32_t)__popcll(wd);
-        const uint32_t incl = wave_prefix_sum(c, lane);
+        const uint32_t incl = wave_prefix_sum(c);
         const uint64_t reach = ballot(incl >= need);
         const int L = reach ? __ffsll((unsigned long long)reach) - 1 : 0;
         const uint32_t r = need - (read_lane(incl, L) - read_lane(c, L));  // 1..64
@@ -398,7 +398,7 @@ __device__ __forceinline__ void order_and_pack(uint32_t e, uint32_t* bmp, uint32
     wave_sync();
     const uint2 wv = reinterpret_cast<const uint2*>(bmp)[lane];
     const uint32_t cnt = (uint32_t)__popcll(((uint64_t)wv.y << 32) | wv.x);
-    pre[lane] = wave_prefix_sum(cnt, lane) - cnt;
+    pre[lane] = wave_prefix_sum(cnt) - cnt;
     wave_sync();
     const uint2 gv = reinterpret_cast<const uint2*>(bmp)[id >> 6];
     const uint64_t gw = ((uint64_t)gv.y << 32) | gv.x;
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(const float* a, cons
         const uint32_t k = key_of(acc[q]);
         mx = k > mx ? k : mx;
     }
-    mx = uniform(wave_max(mx));
+    mx = wave_max(mx);
     clear_shared(sh.hist, kLdsWords, tid);
     if (lane == 0) sh.part_max[w] = mx;
     __syncthreads();

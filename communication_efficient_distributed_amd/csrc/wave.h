@@ -40,33 +40,47 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
+// Cross-lane steps through DPP (data-parallel primitives: a VALU operand
+// taken from another lane of the same wavefront) rather than ds_bpermute,
+// which is an LDS round trip per step.  GFX9 controls: row_shr:n shifts
+// within each row of 16 lanes; row_bcast:15 / row_bcast:31 feed lane 15 / 31
+// to the rows after it.  Lanes whose source falls outside the row, or whose
+// row is masked off, take 0, the identity of both + and max on uint32.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive scan over the 64 lanes (lane l gets op over lanes 0..l): four
+// shift steps within each row of 16, then two broadcasts across rows.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, Op op) {
+    v = op(v, dpp_or_zero<kRowShr1, 0xf>(v));
+    v = op(v, dpp_or_zero<kRowShr2, 0xf>(v));
+    v = op(v, dpp_or_zero<kRowShr4, 0xf>(v));
+    v = op(v, dpp_or_zero<kRowShr8, 0xf>(v));
+    v = op(v, dpp_or_zero<kRowBcast15, 0xa>(v));
+    v = op(v, dpp_or_zero<kRowBcast31, 0xc>(v));
+    return v;
+}
+
+// Inclusive prefix sum over lanes: lane l gets the sum of v over lanes <= l.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v) {
+    return wave_scan(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Inclusive suffix sum over lanes: lane l gets the sum of v over lanes >= l.
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+    const uint32_t incl = wave_prefix_sum(v);
+    return read_lane(incl, kWave - 1) - incl + v;
+}
+
+// Maximum over the wavefront, the same (wave-uniform) value in every lane.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        uint32_t y = (uint32_t)__shfl_xor((int)v, o, kWave);
-        v = v > y ? v : y;
-    }
-    return v;
-}
-
-// Inclusive suffix sum over lanes: lane l gets sum of v over lanes >= l.
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t y = (uint32_t)__shfl_down((int)v, o, kWave);
-        if (lane + o < kWave) v += y;
-    }
-    return v;
-}
-
-// Inclusive prefix sum over lanes: lane l gets sum of v over lanes <= l.
-__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t y = (uint32_t)__shfl_up((int)v, o, kWave);
-        if (lane >= o) v += y;
-    }
-    return v;
+    return read_lane(wave_scan(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; }), kWave - 1);
 }
 
 // LDS atomics at wavefront scope (only lanes of one wavefront touch a slice).
