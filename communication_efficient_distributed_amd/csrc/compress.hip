@@ -11,10 +11,12 @@
 // Wavefront w holds elements 1024 w + 256 m + 4 l + j (m, j = 0..3) in 16
 // registers per lane, so every global load and store instruction touches one
 // contiguous KiB.  The selection's partial results cross wavefronts through
-// 8 KiB of LDS and workgroup barriers; no barrier ties workgroups together.
-// (On 8192 x 28672 parameters four wavefronts per chunk measured 5% faster
-// than one, which needs 167 registers per lane and runs three wavefronts per
-// SIMD; two and eight wavefronts per chunk were slower than four.)
+// LDS (11.3 KiB, a region per phase) and workgroup barriers; no barrier ties
+// workgroups together.  (On 8192 x 28672 parameters four wavefronts per chunk
+// measured 5% faster than one, which needs 167 registers per lane and runs
+// three wavefronts per SIMD; two and eight wavefronts per chunk were slower
+// than four.)  A residency cap keeps at most 6 workgroups on a CU (5 for the
+// weights variant), see the launchers.
 //
 // Selection (exact, deterministic): find the 64th element of the order
 // (|acc| descending, index ascending) -- the "cut" -- by an MSB-first radix
