@@ -40,22 +40,35 @@ BYTES_APPLY = 4 + 4 + 4                               # read theta, out; write t
 
 METRIC = "compressed Gparams/s and % of HBM roofline (compress + 24-peer aggregate)"
 PROFILE = os.path.join(ROOT, "profiles", "compress_mlp_8192x28672_counters.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "communication_efficient_distributed_amd", "csrc", "compress.hip")
+CSRC = os.path.join(ROOT, "communication_efficient_distributed_amd", "csrc")
+# The compressor's device code: its source and every header it includes.
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("compress.hip", "wave.h", "residency.h", "internal.h")] + \
+    [os.path.join(ROOT, "include", "sparseloco.h")]
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def code_digest(paths) -> str:
+    """SHA-256 (16 hex digits) of the given C++ sources with comments removed
+    and whitespace collapsed: a comment edit leaves it unchanged, a code edit
+    does not."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(n_params: int):
     """HBM bytes per compress launch from the committed counter summary, or None
-    if there is none or it was taken on a different compress.hip."""
+    if there is none or it was taken on different compressor code."""
     if not os.path.exists(PROFILE):
         return None
     txt = open(PROFILE).read()
-    m = re.search(r"compress_source_sha256_16:\s*([0-9a-f]{16})", txt)
-    if not m or m.group(1) != source_hash(KERNEL_SOURCE):
+    m = re.search(r"compress_code_sha256_16:\s*([0-9a-f]{16})", txt)
+    if not m or m.group(1) != code_digest(KERNEL_SOURCES):
         return None
     f = re.search(r"compress_hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     p = re.search(r"params_per_launch:\s*(\d+)", txt)

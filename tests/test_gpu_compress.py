@@ -118,6 +118,19 @@ def test_tricky_chunks(orc):
     check_round(sl, orc, d, e, 0.95, "tricky signed-zero ef")
 
 
+@pytest.mark.parametrize("beta", [0.0, 0.5, -0.75, 1.5, float(np.float32(1e-30))])
+def test_other_decays(orc, beta):
+    """Any finite decay: beta = 0 (no memory), a negative beta (products of
+    either sign in the fma), beta > 1 and a tiny beta (beta * ef underflows to
+    denormals or zero), each over three rounds on lognormal chunks."""
+    sl = require_gpu()
+    n = 64 * 4096
+    ef = np.zeros(n, np.float32)
+    for rnd in range(3):
+        d = datagen.lognormal(n, datagen.SMALL_1M, 0, 40 + rnd).numpy()
+        ef = check_round(sl, orc, d, ef, beta, f"beta={beta} round {rnd}")
+
+
 def test_random_small_integer_chunks(orc):
     """Many chunks with values in a tiny integer set: every selection level
     and the index tie-break get exercised at scale."""
