@@ -81,9 +81,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The first ~25 compressor calls of a process run up to 30% slower while
-    # the device settles under sustained load; 30 warmup steps (about 20 ms)
-    # leave the timed steps in the steady state.
+    # After the GPU idles, the first ~25 compressor calls run up to 30% slower
+    # while the device settles under load.  Setup ends with the peers'
+    # compressions, leading straight into the warmup; 30 warmup steps (about
+    # 20 ms) add margin.
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
@@ -122,6 +123,9 @@ def main():
     scales = torch.empty(C, dtype=torch.float32, device=dev)
     out = torch.empty(n, dtype=torch.float32, device=dev)
     theta = datagen.theta0(n, W, dev)
+    # Host copy for the CPU baseline, taken before the peer records are made
+    # so that the GPU goes from that work straight into the warmup steps.
+    ef0_host = ef.cpu().numpy()
     peer_p, peer_s = [], []
     scratch_ef = torch.zeros(n, dtype=torch.float32, device=dev)
     for p in range(1, N_PEERS + 1):
@@ -133,8 +137,6 @@ def main():
         del d
     del scratch_ef
     torch.cuda.synchronize()
-    # Copies kept for the CPU baseline (host side, first sample chunks).
-    ef0_host = ef.cpu().numpy()
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
