@@ -232,3 +232,49 @@ def test_ef_offloaded_to_host(orc):
         assert_bitwise(ef_host.numpy(), ef_o, "host ef")
         assert_bitwise(ef_dev.cpu().numpy(), ef_o, "device ef")
         assert_bitwise(p2.cpu().numpy(), op, "device-ef payload")
+
+
+def test_outer_loop_rounds(orc):
+    """Three outer rounds of five peers, composed as the pages' round runs.
+    Each peer p has its own error feedback. It takes theta, runs a synthetic
+    inner loop (theta_post = theta - step_p) and compresses its
+    pseudo-gradient straight from the weights (sl_compress_weights). The
+    round's records are screened (sl_peer_stats) and applied to theta with
+    the fused update (sl_aggregate_apply), and the next round starts from
+    that theta. Everything is compared with the oracle doing the same,
+    bitwise, every round."""
+    sl = require_gpu()
+    N, C = 5, 48
+    n = C * 4096
+    W = datagen.SMALL_1M
+    theta_o = datagen.theta0(n, W).numpy()
+    theta_g = torch.from_numpy(theta_o).cuda()
+    ef_o = [np.zeros(n, np.float32) for _ in range(N)]
+    ef_g = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(N)]
+    pay_g = [torch.empty((C, 112), dtype=torch.uint8, device="cuda") for _ in range(N)]
+    sc_g = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(N)]
+    counts = torch.empty((N, 4), dtype=torch.int64, device="cuda")
+    smax = torch.empty(N, dtype=torch.float32, device="cuda")
+    for rnd in range(3):
+        pay_o, sc_o = [], []
+        for p in range(N):
+            step = (datagen.lognormal(n, W, p + 1, 50 + rnd).numpy() * np.float32(1e-3)).astype(np.float32)
+            post_o = (theta_o - step).astype(np.float32)
+            pl, s, ef_o[p] = orc.compress(orc.pseudo_gradient(theta_o, post_o), ef_o[p], beta=0.95)
+            pay_o.append(pl)
+            sc_o.append(s)
+            note(f"outer loop round {rnd} peer {p}: sl_compress_weights")
+            sl.sl_compress_weights(theta_g, torch.from_numpy(post_o).cuda(), ef_g[p], 0.95, pay_g[p], sc_g[p])
+        note(f"outer loop round {rnd}: sl_peer_stats + sl_aggregate_apply")
+        sl.sl_peer_stats(pay_g, sc_g, counts, smax)
+        sl.sl_aggregate_apply(pay_g, sc_g, theta_g)
+        theta_o = orc.apply_mean(theta_o, orc.aggregate(pay_o, sc_o, n), N)
+        torch.cuda.synchronize()
+        for p in range(N):
+            assert_bitwise(pay_g[p].cpu().numpy(), pay_o[p], f"round {rnd} peer {p} records")
+            assert_bitwise(sc_g[p].cpu().numpy(), sc_o[p], f"round {rnd} peer {p} scales")
+            assert_bitwise(ef_g[p].cpu().numpy(), ef_o[p], f"round {rnd} peer {p} ef")
+            wc, wm = orc.peer_stats(pay_o[p], sc_o[p])
+            assert counts[p].cpu().tolist() == wc.tolist(), f"round {rnd} peer {p} counts"
+            assert wc[0] == 0                         # the compressor's records are well formed
+        assert_bitwise(theta_g.cpu().numpy(), theta_o, f"round {rnd} theta")
