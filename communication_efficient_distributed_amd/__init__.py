@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     PeerSet,
     SparseLoCoError,
     aggregate,
+    apply_mean,
     compress,
     host_device_pointer,
     load,

@@ -319,6 +319,8 @@ def sl_apply_mean(theta: torch.Tensor, out: torch.Tensor, n_peers: int, stream=N
 # Convenience wrappers that allocate outputs with torch (device memory only).
 
 def compress(delta: torch.Tensor, ef: torch.Tensor, beta: float = 0.95, stream=None):
+    """sl_compress into freshly allocated outputs: returns (payload uint8
+    [n/4096, 112], scales float32 [n/4096]); ef is updated in place."""
     C = delta.numel() // SL_CHUNK
     payload = torch.empty((C, SL_PAYLOAD_BYTES), dtype=torch.uint8, device=delta.device)
     scales = torch.empty(C, dtype=torch.float32, device=delta.device)
@@ -328,6 +330,8 @@ def compress(delta: torch.Tensor, ef: torch.Tensor, beta: float = 0.95, stream=N
 
 def aggregate(payloads, scales=None, n: int | None = None, out: torch.Tensor | None = None,
               stream=None) -> torch.Tensor:
+    """sl_aggregate, allocating out (float32 [n]) unless it is given; n
+    defaults to what the peers' records cover."""
     if out is None:
         if isinstance(payloads, PeerSet):
             if n is None:
@@ -340,3 +344,9 @@ def aggregate(payloads, scales=None, n: int | None = None, out: torch.Tensor | N
         out = torch.empty(n, dtype=torch.float32, device=dev)
     sl_aggregate(payloads, scales, out, stream)
     return out
+
+
+def apply_mean(theta: torch.Tensor, out: torch.Tensor, n_peers: int, stream=None) -> torch.Tensor:
+    """theta <- theta - out / n_peers in place (sl_apply_mean); returns theta."""
+    sl_apply_mean(theta, out, n_peers, stream)
+    return theta

@@ -143,6 +143,8 @@ def test_binding_rejects_host_tensors():
     with pytest.raises((ValueError, TypeError)):
         sl.sl_compress(d, torch.zeros(4096), 0.95, torch.zeros((1, 112), dtype=torch.uint8),
                        torch.zeros(1))
+    with pytest.raises((ValueError, TypeError)):
+        sl.apply_mean(torch.zeros(4096), torch.zeros(4096), 3)
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
