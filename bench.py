@@ -89,6 +89,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip timing the entry points beyond the three-step path")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip timing compress and aggregate at the other workload shapes")
     ap.add_argument("--cpu-sample-chunks", type=int, default=57344)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a torch copy of 1 GiB (for counter calibration)")
@@ -247,6 +249,10 @@ def main():
         result["next_rows"] = next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n,
                                         stream, kstats)
 
+    if not args.no_workloads:
+        del out
+        result["workloads"] = workloads(sl, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n)
 
@@ -303,6 +309,89 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     t = timed(lambda: sl.sl_peer_stats(peers, None, counts, smax, flags=flags_all))
     res["peer_stats_24_peers"] = kstats(t, N_PEERS * (RECORD + 1) / CHUNK)
     res["small_round_1m"] = small_round(sl, delta.device)
+    return res
+
+
+def timed_calls(torch, stream, fn, k=20, warm=3):
+    """Mean and per-call times (ms) of fn, each call timed on its own behind a
+    short spin kernel, so that host-side argument marshalling (pointer tables
+    of 24 peers) is finished before the GPU reaches it: the events see the
+    kernels only."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+    for e0, e1 in evs:
+        torch.cuda._sleep(200000)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return sum(t) / k, t
+
+
+def workloads(sl, dev, reps=10):
+    """Compress and the 24-peer aggregate at the other workload shapes: the
+    1,048,576-parameter case (cache-resident), one 8192 x 8192 projection, one
+    decoder block (also the fused aggregate + update and apply_mean), and the
+    16e9-parameter flat span (skipped when the device lacks the 203 GB it
+    needs).  Every buffer is resident; 24 peers' records come from compressing
+    24 independently seeded pseudo-gradients from ef = 0."""
+    import torch
+
+    from communication_efficient_distributed_amd import datagen
+
+    stream = torch.cuda.current_stream(dev)
+
+    def st(n, t_ms, bpp, samples):
+        gbs = bpp * n / (t_ms * 1e-3) / 1e9
+        return {"ms": round(t_ms, 5), "ms_min": round(min(samples), 5),
+                "gparams_per_s": round(n / (t_ms * 1e-3) / 1e9, 2), "gb_per_s": round(gbs, 1),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_param": round(bpp, 4)}
+
+    res = {}
+    for name, W in (("small_1m", datagen.SMALL_1M), ("attn_8192x8192", datagen.ATTN_8192),
+                    ("decoder_block", datagen.DECODER_BLOCK), ("flat_16b", datagen.FLAT_16B)):
+        n = datagen.WORKLOAD_PARAMS[W]
+        C = n // CHUNK
+        need = 3 * 4 * n + N_PEERS * C * RECORD + (4 << 30)
+        free, _ = torch.cuda.mem_get_info(dev)
+        if free < need:
+            res[name] = {"params": n, "skipped": f"needs {need / 1e9:.0f} GB of free device memory, "
+                                                 f"{free / 1e9:.0f} GB free"}
+            continue
+        a = torch.empty(n, dtype=torch.float32, device=dev)
+        ef = torch.empty(n, dtype=torch.float32, device=dev)
+        pp, ps = [], []
+        for p in range(1, N_PEERS + 1):
+            datagen.fill_lognormal_(a, W, p, 0)
+            ef.zero_()
+            pl, sc = sl.compress(a, ef, BETA)
+            pp.append(pl)
+            ps.append(sc)
+        peers = sl.PeerSet(pp, ps)
+        datagen.fill_lognormal_(a, W, 0, 0)
+        ef.zero_()
+        payload = torch.empty((C, 112), dtype=torch.uint8, device=dev)
+        scales = torch.empty(C, dtype=torch.float32, device=dev)
+        out = torch.empty(n, dtype=torch.float32, device=dev)
+        r = {"params": n, "chunks": C, "peers": N_PEERS}
+        t, ts = timed_calls(torch, stream, lambda: sl.sl_compress(a, ef, BETA, payload, scales), k=reps)
+        r["compress"] = st(n, t, BYTES_COMPRESS, ts)
+        t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate(peers, None, out), k=reps)
+        r["aggregate"] = st(n, t, BYTES_AGGREGATE, ts)
+        if W == datagen.DECODER_BLOCK:
+            theta = ef
+            theta.copy_(a).mul_(0.02)
+            t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate_apply(peers, None, theta), k=reps)
+            r["aggregate_apply_fused"] = st(n, t, 8 + N_PEERS * RECORD / CHUNK, ts)
+            t, ts = timed_calls(torch, stream, lambda: sl.sl_apply_mean(theta, out, N_PEERS), k=reps)
+            r["apply_mean"] = st(n, t, BYTES_APPLY, ts)
+        res[name] = r
+        del a, ef, out, payload, scales, pp, ps, peers
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return res
 
 

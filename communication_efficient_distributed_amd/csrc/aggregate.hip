@@ -22,7 +22,9 @@
 //      updated in place).
 // The fused update for up to 27 peers uses four wavefronts per chunk instead:
 // wavefront 0 runs steps 1-2 while each wavefront loads its own quarter of
-// theta, then each updates its quarter from the tile.
+// theta, then each updates its quarter from the tile.  When a call's records
+// exceed the last-level cache, a wavefront sums three neighbouring chunks in
+// turn, with every chunk's records loaded in step 1.
 //
 // Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
@@ -140,19 +142,22 @@ __device__ __forceinline__ void load_theta(const float* theta_chunk, v4f (&th)[k
     }
 }
 
-// The sums of chunk `chunk` over up to 9 * NGMAX peers, into the LDS tile
-// (cleared here), in ascending peer order; run by one wavefront.  Every record
-// slice of the chunk is loaded into registers up front (NGMAX loads of 16
-// bytes per lane, 9 peers each; lanes past the last peer re-read peer 0, so no
-// load sits in a divergent branch); `issued()` runs once the loads are in
-// flight.  The peers are then staged 9 at a time in `stage` (1.1 KiB).
-template <int NGMAX, typename Issued>
-__device__ __forceinline__ void sum_chunk(const PeerTable& peers, int32_t n_peers, int64_t chunk, float* tile,
-                                          uint32_t* stage, int lane, Issued issued) {
+// One chunk's slices of every peer's record, in registers: lane 7 q + i holds
+// bytes [16 i, 16 i + 16) of peer 9 g + q's record in r[g] (lane 63 and lanes
+// past the last peer re-read peer 0, so no load sits in a divergent branch),
+// and lane q < 9 holds that peer's scale in sv[g].
+template <int NGMAX>
+struct ChunkRecords {
+    v4u r[NGMAX];
+    float sv[NGMAX];
+};
+
+template <int NGMAX>
+__device__ __forceinline__ void load_records(const PeerTable& peers, int32_t n_peers, int64_t chunk, int lane,
+                                             ChunkRecords<NGMAX>& cr) {
     constexpr int kMaxPeers = kPeersPerLoad * NGMAX;
     const int rp = lane / kQuads;
     const int rq = lane - kQuads * rp;
-    const EntryPos pos(lane);
     const size_t off = (size_t)chunk * SL_PAYLOAD_BYTES + 16 * (size_t)rq;
 
     const uint8_t* src[NGMAX];
@@ -165,11 +170,8 @@ __device__ __forceinline__ void sum_chunk(const PeerTable& peers, int32_t n_peer
             if (rp == p % kPeersPerLoad) src[p / kPeersPerLoad] = pp;
         }
     }
-    v4u r[NGMAX];
 #pragma unroll
-    for (int g = 0; g < NGMAX; ++g) r[g] = load_record16(src[g] + off);
-    // lane q < 9: scale of peer 9 g + q (peer 0's for lanes past the last peer)
-    float sv[NGMAX];
+    for (int g = 0; g < NGMAX; ++g) cr.r[g] = load_record16(src[g] + off);
 #pragma unroll
     for (int g = 0; g < NGMAX; ++g) {
         const float* ssrc = peers.scales[0];
@@ -181,38 +183,64 @@ __device__ __forceinline__ void sum_chunk(const PeerTable& peers, int32_t n_peer
                 if (lane == q) ssrc = sp;
             }
         }
-        sv[g] = ssrc[chunk];
+        cr.sv[g] = ssrc[chunk];
     }
-    // With 9 or more loads per lane, wait for all of them here, ahead of the
-    // sums: otherwise the compiler sinks the last load into the group that
-    // consumes it, and its latency lands in the middle of the sums.  (With
-    // fewer loads the staggered issue measured faster.)
-    if constexpr (NGMAX >= 9) {
-#pragma unroll
-        for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(r[g]));
-    }
-    issued();
+}
 
+// Make the compiler wait for every load of cr at this point.
+template <int NGMAX>
+__device__ __forceinline__ void await_records(const ChunkRecords<NGMAX>& cr) {
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(cr.r[g]), "v"(cr.sv[g]));
+}
+
+// The sums of one chunk over up to 9 * NGMAX peers from its loaded records,
+// into the LDS tile (cleared here), in ascending peer order; run by one
+// wavefront.  The peers are staged 9 at a time in `stage` (1.1 KiB).
+template <int NGMAX>
+__device__ __forceinline__ void sum_records(const ChunkRecords<NGMAX>& cr, int32_t n_peers, float* tile,
+                                            uint32_t* stage, int lane) {
+    const int rp = lane / kQuads;
+    const int rq = lane - kQuads * rp;
+    const EntryPos pos(lane);
     const int slot = rp < kPeersPerLoad ? rp : kPeersPerLoad;  // lane 63: dummy slot 9
     clear_tile(tile, lane);
 #pragma unroll
     for (int g = 0; g < NGMAX; ++g) {
         const int p0 = kPeersPerLoad * g;
         if (p0 < n_peers) {
-            *reinterpret_cast<v4u*>(stage + slot * kRecWords + 4 * rq) = r[g];
+            *reinterpret_cast<v4u*>(stage + slot * kRecWords + 4 * rq) = cr.r[g];
             wave_sync();
             uint32_t f[kPeersPerLoad];  // slots past the last peer hold stale bytes, never used
 #pragma unroll
             for (int q = 0; q < kPeersPerLoad; ++q) f[q] = pos.read(stage + q * kRecWords);
-            const float s3v = sv[g] / 3.0f;
+            const float s3v = cr.sv[g] / 3.0f;
             wave_sync();
 #pragma unroll
             for (int q = 0; q < kPeersPerLoad; ++q)
                 if (p0 + q < n_peers)
-                    add_entry(tile, f[q], __uint_as_float(read_lane(__float_as_uint(sv[g]), q)),
+                    add_entry(tile, f[q], __uint_as_float(read_lane(__float_as_uint(cr.sv[g]), q)),
                               __uint_as_float(read_lane(__float_as_uint(s3v), q)));
         }
     }
+}
+
+// The sums of chunk `chunk` into the tile: its records are loaded, `issued()`
+// runs once the loads are in flight, then the sums.  With 9 or more loads per
+// lane every load is awaited ahead of the sums: otherwise the compiler sinks
+// the last load into the group that consumes it, and its latency lands in the
+// middle of the sums.  (With fewer loads the staggered issue measured faster.)
+template <int NGMAX, typename Issued>
+__device__ __forceinline__ void sum_chunk(const PeerTable& peers, int32_t n_peers, int64_t chunk, float* tile,
+                                          uint32_t* stage, int lane, Issued issued) {
+    ChunkRecords<NGMAX> cr;
+    load_records<NGMAX>(peers, n_peers, chunk, lane, cr);
+    if constexpr (NGMAX >= 9) {
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(cr.r[g]));
+    }
+    issued();
+    sum_records<NGMAX>(cr, n_peers, tile, stage, lane);
 }
 
 // One chunk per workgroup of one wavefront.  The tile keeps the partial sums:
@@ -243,6 +271,55 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
     wave_sync();
     finish_chunk<APPLY>(tile, dst_chunk, th, nf, lane);
 }
+
+// CPW neighbouring chunks per wavefront, for records that come from HBM.
+// Every chunk's records are loaded up front, so the later chunks' arrive while
+// the first is summed; they are awaited before the first chunk's stores are
+// issued, so that no wait on a load covers any store.  Each chunk goes through
+// the same operations, in the same order, as in aggregate_kernel.
+template <int NGMAX, int CPW>
+__global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, int32_t n_peers, float* out,
+                                                              int64_t n_chunks, int64_t per_xcd) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t c0 = CPW * xcd_chunk(per_xcd);
+    if (c0 >= n_chunks) return;
+    const int64_t count = n_chunks - c0 < CPW ? n_chunks - c0 : CPW;  // the same in every lane
+    ChunkRecords<NGMAX> cr[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) load_records<NGMAX>(peers, n_peers, i < count ? c0 + i : c0, lane, cr[i]);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        if (i < count) {
+            sum_records<NGMAX>(cr[i], n_peers, tile, stage, lane);
+            if (i == 0) {
+#pragma unroll
+                for (int j = 1; j < CPW; ++j) await_records<NGMAX>(cr[j]);
+            }
+            wave_sync();
+            store_tile(tile, out + (size_t)(c0 + i) * SL_CHUNK, lane);
+        }
+    }
+}
+
+// The run kernel is used when a launch's records and scales exceed the
+// last-level cache (256 MB on MI355X): they then come from HBM, and the later
+// chunks' loads hide that latency.  Records that fit are likely still cached
+// from the step that received or validated them; there one chunk per
+// wavefront is as fast or faster (8192 x 28672 parameters, 24 peers: 156 us
+// against 168 us for two chunks per wavefront).  Measured beyond the cache
+// (one chunk per wavefront / two / three / four):
+//   decoder block, 24 peers       0.82-0.86   0.75-0.77   0.72-0.75   0.75-0.76 ms
+//   decoder block, 48 peers       1.01-1.02   0.88        0.80-0.81   0.83-0.84 ms
+//   8192 x 28672, 48 peers        0.23        0.19        0.185-0.187 0.194 ms
+//   16e9 parameters, 24 peers     15.0-15.2   12.3-12.5   12.0-13.3   11.8 ms
+// Three chunks per wavefront hold 98 registers per lane at 24 peers and 151 at
+// 54; beyond 54 peers the records of three chunks would not fit, and the
+// one-chunk kernel is used.
+constexpr uint64_t kCachedRecordBytes = 256ull << 20;
+constexpr int kChunksPerWave = 3;
+constexpr int kRunMaxPeers = kPeersPerLoad * 6;
 
 // Fused outer update with four wavefronts per chunk: wavefront 0 sums the
 // peers into the tile as above, while every wavefront w loads its own
@@ -333,9 +410,10 @@ __global__ __launch_bounds__(kWave * kMeanWaves) void apply_mean_kernel(float* t
 constexpr int kCapApplyMean = 3;
 static_assert(cap_is_exact(kCapApplyMean, 0), "residency cap");
 
+// One launch over chunks [0, n_chunks) of the given buffers.
 template <bool APPLY>
-hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float* dst,
-                                 int64_t n_chunks, hipStream_t stream) {
+hipError_t launch_aggregate_one(const PeerTable& peers, int32_t n_peers, float* dst,
+                                int64_t n_chunks, hipStream_t stream) {
     PeerTable t = peers;
     float nf = (float)n_peers;
     int64_t per_xcd = (n_chunks + kXcds - 1) / kXcds;
@@ -368,7 +446,39 @@ hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float*
             return hipLaunchKernel(k4, grid, dim3(kWave * kApplyWaves), args, residency_lds(cap, kStatic), stream);
         }
     }
+    if constexpr (!APPLY) {
+        if (n_peers <= kRunMaxPeers &&
+            (uint64_t)n_peers * (uint64_t)n_chunks * (SL_PAYLOAD_BYTES + sizeof(float)) > kCachedRecordBytes) {
+            const int64_t runs = (n_chunks + kChunksPerWave - 1) / kChunksPerWave;
+            int64_t run_per_xcd = (runs + kXcds - 1) / kXcds;
+            void* pargs[] = {(void*)&t, (void*)&n_peers, (void*)&dst, (void*)&n_chunks, (void*)&run_per_xcd};
+            constexpr int R = kChunksPerWave;
+            const void* kp = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_run_kernel<1, R>)
+                             : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_run_kernel<2, R>)
+                             : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_run_kernel<3, R>)
+                                                            : reinterpret_cast<const void*>(&aggregate_run_kernel<6, R>);
+            return hipLaunchKernel(kp, dim3((unsigned)(run_per_xcd * kXcds)), dim3(kWave), pargs, 0, stream);
+        }
+    }
     return hipLaunchKernel(k, grid, dim3(kWave), args, 0, stream);
+}
+
+// One launch per kLaunchChunks chunks, each on its own slice of the records,
+// scales and dense buffer.
+template <bool APPLY>
+hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float* dst,
+                                 int64_t n_chunks, hipStream_t stream) {
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
+        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+        PeerTable t = {};
+        for (int32_t p = 0; p < n_peers; ++p) {
+            t.payload[p] = peers.payload[p] + (size_t)c0 * SL_PAYLOAD_BYTES;
+            t.scales[p] = peers.scales[p] + c0;
+        }
+        const hipError_t e = launch_aggregate_one<APPLY>(t, n_peers, dst + (size_t)c0 * SL_CHUNK, m, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -385,11 +495,18 @@ hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float
 
 hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,
                              hipStream_t stream) {
-    int64_t n_chunks = n / SL_CHUNK;
+    const int64_t n_chunks = n / SL_CHUNK;
     float nf = (float)n_peers;
-    void* args[] = {(void*)&theta, (void*)&out, (void*)&nf, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&apply_mean_kernel), dim3((unsigned)n_chunks),
-                           dim3(kWave * kMeanWaves), args, residency_lds(kCapApplyMean, 0), stream);
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
+        int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+        float* st = theta + (size_t)c0 * SL_CHUNK;
+        const float* so = out + (size_t)c0 * SL_CHUNK;
+        void* args[] = {(void*)&st, (void*)&so, (void*)&nf, (void*)&m};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&apply_mean_kernel), dim3((unsigned)m),
+                                             dim3(kWave * kMeanWaves), args, residency_lds(kCapApplyMean, 0), stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace sl

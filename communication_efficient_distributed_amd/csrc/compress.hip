@@ -504,24 +504,38 @@ constexpr int kCapWeights = 5;
 static_assert(cap_is_exact(kCapCompress, sizeof(Shared)) && cap_is_exact(kCapWeights, sizeof(Shared)),
               "residency caps");
 
+// One launch per kLaunchChunks chunks, each on its own slice of every buffer.
+template <bool WEIGHTS>
+hipError_t launch_segments(const float* a, const float* b, float* ef, float beta, uint8_t* payload, float* scales,
+                           int64_t n_chunks, int cap, hipStream_t stream) {
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
+        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+        const size_t e0 = (size_t)c0 * SL_CHUNK;
+        const float* sa = a + e0;
+        const float* sb = WEIGHTS ? b + e0 : b;
+        float* sef = ef + e0;
+        uint8_t* sp = payload + (size_t)c0 * SL_PAYLOAD_BYTES;
+        float* ss = scales + c0;
+        void* args[] = {(void*)&sa, (void*)&sb, (void*)&sef, (void*)&beta, (void*)&sp, (void*)&ss, (void*)&m};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel<WEIGHTS>),
+                                             dim3((unsigned)m), dim3(kThreads), args, residency_lds(cap, sizeof(Shared)),
+                                             stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
                                    float beta, uint8_t* payload, float* scales, int64_t n_chunks,
                                    hipStream_t stream) {
-    void* args[] = {(void*)&theta_pre, (void*)&theta_post, (void*)&ef, (void*)&beta,
-                    (void*)&payload, (void*)&scales, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel<true>), dim3((unsigned)n_chunks),
-                           dim3(kThreads), args, residency_lds(kCapWeights, sizeof(Shared)), stream);
+    return launch_segments<true>(theta_pre, theta_post, ef, beta, payload, scales, n_chunks, kCapWeights, stream);
 }
 
 hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* payload,
                            float* scales, int64_t n_chunks, hipStream_t stream) {
-    const float* unused = nullptr;
-    void* args[] = {(void*)&delta, (void*)&unused, (void*)&ef, (void*)&beta, (void*)&payload,
-                    (void*)&scales, (void*)&n_chunks};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&compress_kernel<false>), dim3((unsigned)n_chunks),
-                           dim3(kThreads), args, residency_lds(kCapCompress, sizeof(Shared)), stream);
+    return launch_segments<false>(delta, nullptr, ef, beta, payload, scales, n_chunks, kCapCompress, stream);
 }
 
 }  // namespace sl

@@ -9,6 +9,13 @@
 
 namespace sl {
 
+// Chunks per kernel launch.  A launch's work-items along x must fit in 32
+// bits, which at 256 lanes per workgroup allows fewer than 2^24 chunks; larger
+// spans are therefore split into launches of at most 2^22 chunks (17.2e9
+// parameters).  Every output depends on its own chunk only, so the split
+// changes no result.
+constexpr int64_t kLaunchChunks = int64_t(1) << 22;
+
 // Pointer table passed by value in the kernel arguments (2 KiB).
 struct PeerTable {
     const uint8_t* payload[SL_MAX_PEERS];

@@ -250,3 +250,40 @@ def test_peerset_matches_lists_and_follows_buffer_contents(orc):
     torch.cuda.synchronize()
     assert_bitwise(t.cpu().numpy(), orc.apply_mean(theta, want2, N), "fused via PeerSet")
     assert not flags.cpu().numpy().any()
+
+
+# Records beyond the last-level cache (more than 256 MiB of records and scales
+# in one call) are summed three chunks per wavefront for up to 54 peers.  Peer
+# counts at both ends of every variant of that kernel, and beyond it; chunk
+# counts leave the last wavefront one or two chunks.
+@pytest.mark.parametrize("n_peers", [9, 10, 18, 19, 27, 28, 54, 55, 128])
+def test_records_beyond_cache(orc, n_peers):
+    sl = require_gpu()
+    C = (256 << 20) // (n_peers * 116) + 1001
+    C += 1 + n_peers % 2 - C % 3
+    n = C * 4096
+    idx, code, s0 = datagen.random_entries_bulk(C, seed=4000 + n_peers)
+    base = orc.pack(idx, code)
+    del idx, code
+    rng = np.random.default_rng(n_peers)
+    sample = np.unique(np.r_[0, 1, 2, C - 3, C - 2, C - 1, rng.choice(C, 300, replace=False)])
+    pay_g, sc_g, pay_o, sc_o = [], [], [], []
+    for p in range(n_peers):
+        shift = (7919 * p) % C
+        pl = np.roll(base, shift, axis=0)
+        sc = np.roll(s0, shift) * np.float32(1.0 + p / 8.0)
+        pay_g.append(torch.from_numpy(pl).cuda())
+        sc_g.append(torch.from_numpy(sc).cuda())
+        pay_o.append(pl[sample])
+        sc_o.append(sc[sample])
+        del pl
+    assert n_peers * C * 116 > 256 << 20
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    note(f"sl_aggregate beyond the cache: n_peers={n_peers} chunks={C}")
+    sl.sl_aggregate(pay_g, sc_g, out)
+    torch.cuda.synchronize()
+    i = torch.from_numpy(sample).cuda()
+    g = out.view(-1, 4096).index_select(0, i).cpu().numpy().reshape(-1)
+    o = orc.aggregate(pay_o, sc_o, sample.size * 4096, nthreads=oracle_threads())
+    assert_bitwise(g, o, f"aggregate beyond cache, {n_peers} peers")
+    assert not torch.isnan(out).any().item(), "an output chunk was not written"

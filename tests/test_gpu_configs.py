@@ -217,3 +217,84 @@ def test_flat_16b_span_sampled(orc):
     g = gather(out, idx).reshape(-1)
     assert_rel(g, o, "16B aggregate")
     assert_bitwise(g, o, "16B aggregate")
+
+
+def test_span_split_over_launches_sampled(orc):
+    """A span of 2^22 + 3 chunks (17.2e9 parameters), one chunk past where the
+    library splits a call into several kernel launches: compress (two rounds),
+    compress from weights, 2-peer aggregate, fused aggregate-apply and
+    apply_mean, compared with the oracle on sampled chunks that include both
+    sides of the split."""
+    sl = require_gpu()
+    W = datagen.FLAT_16B
+    K = 1 << 22
+    C = K + 3
+    n = C * CHUNK
+    need = 2 * 4 * n + 3 * C * 116 + (8 << 30)   # two dense buffers, records, slack
+    if _free_gpu_bytes() < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory")
+    T = oracle_threads()
+    dev = torch.device("cuda:0")
+    idx = sample_chunks(C, [0, 1, K - 2, K - 1, K, K + 1, K + 2], 512, seed=7)
+    m = idx.size
+
+    a = torch.empty(n, dtype=torch.float32, device=dev)
+    ef = torch.zeros(n, dtype=torch.float32, device=dev)
+    ef_o = np.zeros(m * CHUNK, np.float32)
+    factors = datagen.group_factors(n, W, 0, dev)
+    for rnd in range(2):
+        datagen.fill_lognormal_(a, W, 0, 0x100 + rnd, factors=factors)
+        note(f"split span round {rnd}: sl_compress n={n}")
+        payload, scales = sl.compress(a, ef, 0.95)
+        torch.cuda.synchronize()
+        op, os_, ef_o = orc.compress(gather(a, idx).reshape(-1), ef_o, beta=0.95, nthreads=T, inplace=True)
+        assert_bitwise(gather_rows(payload, idx), op, f"round {rnd} payload")
+        assert_bitwise(gather_rows(scales, idx), os_, f"round {rnd} scales")
+        assert_bitwise(gather(ef, idx).reshape(-1), ef_o, f"round {rnd} ef")
+
+    # Weights variant with theta_pre and theta_post the same buffer: delta is 0
+    # at every chunk only if both are sliced alike for every launch.
+    datagen.fill_lognormal_(a, W, 0, 0x102, factors=factors)
+    note("split span: sl_compress_weights (theta_pre aliases theta_post)")
+    sl.sl_compress_weights(a, a, ef, 0.95, payload, scales)
+    torch.cuda.synchronize()
+    th = gather(a, idx).reshape(-1)
+    op, os_, ef_o = orc.compress(orc.pseudo_gradient(th, th), ef_o, beta=0.95, nthreads=T, inplace=True)
+    assert_bitwise(gather_rows(payload, idx), op, "weights payload")
+    assert_bitwise(gather_rows(scales, idx), os_, "weights scales")
+    assert_bitwise(gather(ef, idx).reshape(-1), ef_o, "weights ef")
+    del payload, scales, factors
+
+    peer_p, peer_s, orc_p, orc_s = [], [], [], []
+    for p in (1, 2):
+        datagen.fill_lognormal_(a, W, p, 0x100)
+        ef.zero_()
+        note(f"split span peer {p}: sl_compress")
+        pl, s = sl.compress(a, ef, 0.95)
+        peer_p.append(pl)
+        peer_s.append(s)
+        op, os_, _ = orc.compress(gather(a, idx).reshape(-1), np.zeros(m * CHUNK, np.float32),
+                                  beta=0.95, nthreads=T)
+        orc_p.append(op)
+        orc_s.append(os_)
+
+    out = ef
+    note("split span: sl_aggregate 2 peers")
+    sl.sl_aggregate(peer_p, peer_s, out)
+    torch.cuda.synchronize()
+    o = orc.aggregate(orc_p, orc_s, m * CHUNK, nthreads=T)
+    assert_bitwise(gather(out, idx).reshape(-1), o, "split aggregate")
+
+    theta = a
+    datagen.fill_lognormal_(theta, W, 0, 0x103)
+    th0 = gather(theta, idx).reshape(-1)
+    note("split span: sl_aggregate_apply 2 peers")
+    sl.sl_aggregate_apply(peer_p, peer_s, theta)
+    torch.cuda.synchronize()
+    th1 = orc.apply_mean(th0, o, 2)
+    assert_bitwise(gather(theta, idx).reshape(-1), th1, "split aggregate_apply")
+
+    note("split span: sl_apply_mean")
+    sl.sl_apply_mean(theta, out, 2)
+    torch.cuda.synchronize()
+    assert_bitwise(gather(theta, idx).reshape(-1), orc.apply_mean(th1, o, 2), "split apply_mean")
