@@ -23,8 +23,8 @@
 // The fused update for up to 27 peers uses four wavefronts per chunk instead:
 // wavefront 0 runs steps 1-2 while each wavefront loads its own quarter of
 // theta, then each updates its quarter from the tile.  When a call's records
-// exceed the last-level cache, a wavefront sums three neighbouring chunks in
-// turn, with every chunk's records loaded in step 1.
+// are too large to stay in the last-level cache, a wavefront sums three
+// neighbouring chunks in turn, with every chunk's records loaded in step 1.
 //
 // Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
@@ -303,21 +303,23 @@ __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, i
     }
 }
 
-// The run kernel is used when a launch's records and scales exceed the
-// last-level cache (256 MB on MI355X): they then come from HBM, and the later
-// chunks' loads hide that latency.  Records that fit are likely still cached
-// from the step that received or validated them; there one chunk per
-// wavefront is as fast or faster (8192 x 28672 parameters, 24 peers: 156 us
-// against 168 us for two chunks per wavefront).  Measured beyond the cache
-// (one chunk per wavefront / two / three / four):
-//   decoder block, 24 peers       0.82-0.86   0.75-0.77   0.72-0.75   0.75-0.76 ms
-//   decoder block, 48 peers       1.01-1.02   0.88        0.80-0.81   0.83-0.84 ms
-//   8192 x 28672, 48 peers        0.23        0.19        0.185-0.187 0.194 ms
-//   16e9 parameters, 24 peers     15.0-15.2   12.3-12.5   12.0-13.3   11.8 ms
+// The run kernel is used when a launch's records and scales exceed 224 MiB,
+// about what the 256 MB last-level cache keeps of them between calls: they
+// then come from HBM, and the later chunks' loads hide that latency.  Records
+// that fit are likely still cached from the step that received or validated
+// them; there one chunk per wavefront is faster.  On 8192 x 28672 parameters
+// with distinct records per peer, one chunk per wavefront against three:
+//   1-27 peers (up to 180 MB)   152-159 us   against 169-181 us
+//   32 peers (213 MB)           173-175 us   against 178-179 us
+//   36 peers (239 MB)           267-268 us   against 234-236 us
+//   40 / 48 peers               274-276 / 307 us   against 257 / 259-260 us
+// and, one / two / three / four chunks per wavefront, 24 peers:
+//   decoder block (582 MB)      0.82-0.86   0.75-0.77   0.72-0.75   0.75-0.76 ms
+//   16e9 parameters (10.9 GB)   15.0-15.2   12.3-12.5   12.0-13.3   11.8 ms
 // Three chunks per wavefront hold 98 registers per lane at 24 peers and 151 at
 // 54; beyond 54 peers the records of three chunks would not fit, and the
 // one-chunk kernel is used.
-constexpr uint64_t kCachedRecordBytes = 256ull << 20;
+constexpr uint64_t kCachedRecordBytes = 224ull << 20;
 constexpr int kChunksPerWave = 3;
 constexpr int kRunMaxPeers = kPeersPerLoad * 6;
 

@@ -252,14 +252,14 @@ def test_peerset_matches_lists_and_follows_buffer_contents(orc):
     assert not flags.cpu().numpy().any()
 
 
-# Records beyond the last-level cache (more than 256 MiB of records and scales
-# in one call) are summed three chunks per wavefront for up to 54 peers.  Peer
+# Records too large for the last-level cache (more than 224 MiB of records and
+# scales in one call) are summed three chunks per wavefront for up to 54 peers.  Peer
 # counts at both ends of every variant of that kernel, and beyond it; chunk
 # counts leave the last wavefront one or two chunks.
 @pytest.mark.parametrize("n_peers", [9, 10, 18, 19, 27, 28, 54, 55, 128])
 def test_records_beyond_cache(orc, n_peers):
     sl = require_gpu()
-    C = (256 << 20) // (n_peers * 116) + 1001
+    C = (224 << 20) // (n_peers * 116) + 1001
     C += 1 + n_peers % 2 - C % 3
     n = C * 4096
     idx, code, s0 = datagen.random_entries_bulk(C, seed=4000 + n_peers)
@@ -277,7 +277,7 @@ def test_records_beyond_cache(orc, n_peers):
         pay_o.append(pl[sample])
         sc_o.append(sc[sample])
         del pl
-    assert n_peers * C * 116 > 256 << 20
+    assert n_peers * C * 116 > 224 << 20
     out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
     note(f"sl_aggregate beyond the cache: n_peers={n_peers} chunks={C}")
     sl.sl_aggregate(pay_g, sc_g, out)
