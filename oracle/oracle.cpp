@@ -38,6 +38,11 @@
  *   R8 ef <- acc - decoded at kept positions, acc elsewhere.
  *   R9 aggregation returns the sum, from +0.0, peers in ascending order.
  *   R10 outer update theta <- theta - sum / N (correctly rounded division).
+ *   R11 pseudo-gradient delta = theta_pre - theta_post, one fp32 subtraction
+ *       ([SF], "Why DiLoCo Alone Isn't Enough": the difference of the weights
+ *       before and after the inner loop; the sign is the reading).
+ *   R12 a well-formed record has strictly increasing indices and a finite,
+ *       non-negative scale (-0 accepted).
  *   R13 per-peer statistics for anomaly screening ([SF], "What the Blockchain
  *       Does (and Doesn't Do)": a crafted sparse update stands out to anomaly
  *       detection): records flagged by the validator, records with a zero
@@ -272,7 +277,7 @@ int orc_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n) {
 
 int64_t orc_validate(const uint8_t* payload, const float* scales, int64_t n_chunks,
                      uint8_t* bad) {
-    /* Reading of a well-formed record: strictly increasing indices, finite and
+    /* R12, a well-formed record: strictly increasing indices, finite and
      * non-negative scale.  bad[c]: bit 0 order, bit 1 non-finite, bit 2 negative. */
     int64_t n_bad = 0;
     int32_t idx[kTopK];
@@ -321,7 +326,7 @@ void orc_peer_stats(const uint8_t* payload, const float* scales, int64_t n_chunk
 void orc_pseudo_gradient(const float* theta_pre, const float* theta_post, int64_t n,
                          float* delta) {
     /* [SF] "Why DiLoCo Alone Isn't Enough": the pseudo-gradient is the difference
-     * between the pre- and post-inner-loop weights; reading: pre - post. */
+     * between the pre- and post-inner-loop weights; R11: pre - post. */
     for (int64_t i = 0; i < n; ++i) delta[i] = theta_pre[i] - theta_post[i];
 }
 
