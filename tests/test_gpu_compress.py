@@ -238,3 +238,49 @@ def test_non_finite_chunks_stay_in_bounds(orc):
     ob = obuf.cpu().numpy()
     assert (ob[:G].view(np.uint32) == sentinel.view(np.uint32)).all()
     assert (ob[G + n:].view(np.uint32) == sentinel.view(np.uint32)).all()
+
+
+def _structured_chunks(rng, n_chunks):
+    """Chunks built to land the cut in every selection path: a small set of
+    magnitudes (some a few ulps apart, some sharing the upper 13 or 23 key
+    bits), each repeated at random indices spread over the whole chunk, over a
+    quieter background, with random signs and signed zeros."""
+    out = np.empty((n_chunks, 4096), np.float32)
+    for c in range(n_chunks):
+        base = np.float32(np.exp(rng.uniform(-20, 20)))
+        bits = np.uint32(base.view(np.uint32))
+        kind = c % 4
+        if kind == 0:      # levels a few ulps apart: resolved by the last key bits
+            offs = rng.integers(0, 8, 6)
+        elif kind == 1:    # same exponent and 3 mantissa bits, differing in bits 19..10
+            offs = rng.integers(0, 1 << 20, 6) & ~np.int64(0x3ff)
+        elif kind == 2:    # differing anywhere in the low 20 bits
+            offs = rng.integers(0, 1 << 20, 6)
+        else:              # one repeated magnitude: index order decides
+            offs = np.zeros(6, np.int64)
+        levels = (bits + offs.astype(np.uint32)).view(np.float32)
+        counts = rng.integers(0, 40, 6)
+        bg_scale = np.float32(base * np.float32(rng.choice([0.0, 1e-3, 0.5, 0.99])))
+        row = (rng.standard_normal(4096).astype(np.float32) * bg_scale).astype(np.float32)
+        if rng.random() < 0.3:
+            row[:] = bg_scale          # a flat background: ties below the levels
+        pos = rng.permutation(4096)
+        k = 0
+        for lv, cnt in zip(levels, counts):
+            row[pos[k:k + cnt]] = lv
+            k += cnt
+        row *= np.where(rng.random(4096) < 0.5, np.float32(-1), np.float32(1))
+        row[rng.random(4096) < 0.01] = -0.0
+        out[c] = row
+    return out.reshape(-1)
+
+
+def test_structured_selection_paths(orc):
+    """2048 structured chunks over two rounds (beta 0.95, then beta 1 on the
+    evolved ef), bitwise against the oracle."""
+    sl = require_gpu()
+    rng = np.random.default_rng(2024)
+    d = _structured_chunks(rng, 2048)
+    ef = np.zeros_like(d)
+    ef = check_round(sl, orc, d, ef, 0.95, "structured round 0")
+    check_round(sl, orc, _structured_chunks(rng, 2048), ef, 1.0, "structured round 1")
