@@ -287,3 +287,45 @@ def test_peerset_checks_once_and_rejects_bad_tensors():
         sl.PeerSet([torch.zeros((4, 112), dtype=torch.uint8)], [])                     # lengths differ
     empty = sl.PeerSet([], [])
     assert len(empty) == 0 and empty.n_chunks == 0
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "sparseloco.h"
+
+/* A plain C99 caller: argument errors come back before any device work. */
+int main(void) {
+    float* fake = (float*)(unsigned long)0x10000;        /* never dereferenced */
+    uint8_t* fake8 = (uint8_t*)(unsigned long)0x20000;
+    const uint8_t* pp[1] = {fake8};
+    const float* sp[1] = {fake};
+    int bad = 0;
+    bad |= sl_compress(fake, fake, 0.95f, fake8, fake, 4095, NULL) != SL_ERR_SHAPE;
+    bad |= sl_compress(NULL, fake, 0.95f, fake8, fake, 4096, NULL) != SL_ERR_INVALID_ARG;
+    bad |= sl_compress(fake, fake, 0.95f, fake8 + 1, fake, 4096, NULL) != SL_ERR_ALIGN;
+    bad |= sl_compress(fake, fake, 0.95f, fake8, fake, 0, NULL) != SL_OK;
+    bad |= sl_aggregate(pp, sp, SL_MAX_PEERS + 1, fake, 4096, NULL) != SL_ERR_TOO_MANY_PEERS;
+    bad |= sl_aggregate_apply(pp, sp, 0, fake, 4096, NULL) != SL_ERR_TOO_MANY_PEERS;
+    bad |= sl_apply_mean(fake, fake, 1, 4096, NULL) != SL_ERR_INVALID_ARG;      /* theta aliases out */
+    bad |= sl_validate_payloads(pp, sp, 1, -1, fake8, NULL) != SL_ERR_SHAPE;
+    bad |= strncmp(sl_status_string(SL_ERR_ALIGN), "SL_ERR_ALIGN", 12) != 0;
+    printf("%s %d\n", bad ? "FAIL" : "OK", SL_PAYLOAD_BYTES);
+    return bad;
+}
+"""
+
+
+def test_header_compiles_as_c99_and_links(lib, tmp_path):
+    """include/sparseloco.h is a plain C header: a C99 program includes it with
+    warnings as errors, links libsparseloco.so without torch or Python, and gets
+    the documented status codes for bad arguments."""
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(lib._name)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                    os.path.join(ROOT, "include"), str(src), "-L", libdir, "-lsparseloco",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.split() == ["OK", "112"], (out.stdout, out.stderr)
