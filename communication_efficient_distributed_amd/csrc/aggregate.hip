@@ -23,8 +23,9 @@
 // The fused update for up to 27 peers uses four wavefronts per chunk instead:
 // wavefront 0 runs steps 1-2 while each wavefront loads its own quarter of
 // theta, then each updates its quarter from the tile.  When a call's records
-// are too large to stay in the last-level cache, a wavefront sums three
-// neighbouring chunks in turn, with every chunk's records loaded in step 1.
+// are too large to stay in the last-level cache, a wavefront sums three (up to
+// 54 peers) or two (up to 81) neighbouring chunks in turn, with every chunk's
+// records loaded in step 1.
 //
 // Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
@@ -317,11 +318,14 @@ __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, i
 //   decoder block (582 MB)      0.82-0.86   0.75-0.77   0.72-0.75   0.75-0.76 ms
 //   16e9 parameters (10.9 GB)   15.0-15.2   12.3-12.5   12.0-13.3   11.8 ms
 // Three chunks per wavefront hold 98 registers per lane at 24 peers and 151 at
-// 54; beyond 54 peers the records of three chunks would not fit, and the
-// one-chunk kernel is used.
+// 54.  From 55 to 81 peers two chunks per wavefront (147 registers) measured
+// 300-363 us against 330-373 us for one (55-81 peers at 8192 x 28672).
+// Beyond 81 peers two chunks' records need 256 registers and took 637-830 us
+// against 464-562 us, so the one-chunk kernel is used.
 constexpr uint64_t kCachedRecordBytes = 224ull << 20;
 constexpr int kChunksPerWave = 3;
-constexpr int kRunMaxPeers = kPeersPerLoad * 6;
+constexpr int kRunMaxPeers = kPeersPerLoad * 6;       // three chunks per wavefront up to here
+constexpr int kPairMaxPeers = kPeersPerLoad * 9;      // two chunks per wavefront up to here
 
 // Fused outer update with four wavefronts per chunk: wavefront 0 sums the
 // peers into the tile as above, while every wavefront w loads its own
@@ -449,16 +453,18 @@ hipError_t launch_aggregate_one(const PeerTable& peers, int32_t n_peers, float* 
         }
     }
     if constexpr (!APPLY) {
-        if (n_peers <= kRunMaxPeers &&
+        if (n_peers <= kPairMaxPeers &&
             (uint64_t)n_peers * (uint64_t)n_chunks * (SL_PAYLOAD_BYTES + sizeof(float)) > kCachedRecordBytes) {
-            const int64_t runs = (n_chunks + kChunksPerWave - 1) / kChunksPerWave;
+            const int R = n_peers <= kRunMaxPeers ? kChunksPerWave : 2;
+            const int64_t runs = (n_chunks + R - 1) / R;
             int64_t run_per_xcd = (runs + kXcds - 1) / kXcds;
             void* pargs[] = {(void*)&t, (void*)&n_peers, (void*)&dst, (void*)&n_chunks, (void*)&run_per_xcd};
-            constexpr int R = kChunksPerWave;
-            const void* kp = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_run_kernel<1, R>)
-                             : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_run_kernel<2, R>)
-                             : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_run_kernel<3, R>)
-                                                            : reinterpret_cast<const void*>(&aggregate_run_kernel<6, R>);
+            constexpr int R3 = kChunksPerWave;
+            const void* kp = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_run_kernel<1, R3>)
+                             : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_run_kernel<2, R3>)
+                             : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_run_kernel<3, R3>)
+                             : n_peers <= kRunMaxPeers      ? reinterpret_cast<const void*>(&aggregate_run_kernel<6, R3>)
+                                                            : reinterpret_cast<const void*>(&aggregate_run_kernel<9, 2>);
             return hipLaunchKernel(kp, dim3((unsigned)(run_per_xcd * kXcds)), dim3(kWave), pargs, 0, stream);
         }
     }

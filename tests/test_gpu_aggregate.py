@@ -253,14 +253,15 @@ def test_peerset_matches_lists_and_follows_buffer_contents(orc):
 
 
 # Records too large for the last-level cache (more than 224 MiB of records and
-# scales in one call) are summed three chunks per wavefront for up to 54 peers.  Peer
-# counts at both ends of every variant of that kernel, and beyond it; chunk
-# counts leave the last wavefront one or two chunks.
-@pytest.mark.parametrize("n_peers", [9, 10, 18, 19, 27, 28, 54, 55, 128])
+# scales in one call) are summed three chunks per wavefront up to 54 peers and
+# two up to 81.  Peer counts at both ends of every variant of that kernel, and
+# beyond it; odd chunk counts, one or two past a multiple of three, leave the
+# last wavefront a partial run.
+@pytest.mark.parametrize("n_peers", [9, 10, 18, 19, 27, 28, 54, 55, 81, 82, 128])
 def test_records_beyond_cache(orc, n_peers):
     sl = require_gpu()
     C = (224 << 20) // (n_peers * 116) + 1001
-    C += 1 + n_peers % 2 - C % 3
+    C += (1 if n_peers % 2 else 5) - C % 6
     n = C * 4096
     idx, code, s0 = datagen.random_entries_bulk(C, seed=4000 + n_peers)
     base = orc.pack(idx, code)
