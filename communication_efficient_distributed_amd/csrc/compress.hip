@@ -433,11 +433,11 @@ __device__ __forceinline__ void order_and_pack(uint32_t e, uint32_t* bmp, uint32
     if (lane < SL_PAYLOAD_BYTES / 4) reinterpret_cast<uint32_t*>(record)[lane] = word;
 }
 
-// One chunk per workgroup.  WEIGHTS: the pseudo-gradient is formed on the fly
-// as a - b with one fp32 subtraction (a = theta_pre, b = theta_post; "Why
-// DiLoCo Alone Isn't Enough" in "The Sparse Frontier" defines it as the
-// difference between the pre- and post-inner-loop weights); otherwise a is
-// delta and b is unused.  Then acc = beta * ef + delta with one rounding.
+// One chunk per workgroup.  WEIGHTS: delta = a - b is formed on the fly with
+// one fp32 subtraction, a = theta_pre and b = theta_post (pseudo-gradient as in
+// "The Sparse Frontier", section "Why DiLoCo Alone Isn't Enough"; the sign,
+// pre minus post, is a reading); otherwise a is delta and b is unused.  Then
+// acc = beta * ef + delta with one rounding.
 template <bool WEIGHTS>
 __global__ __launch_bounds__(kThreads) void compress_kernel(const float* a, const float* b, float* ef, float beta,
                                                             uint8_t* payload, float* scales, int64_t n_chunks) {

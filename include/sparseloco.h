@@ -11,9 +11,10 @@
  * Conventions for every entry point:
  *  - All buffer pointers are DEVICE pointers owned by the caller.  The library
  *    allocates nothing, keeps no state between calls and is reentrant.
- *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *    on it and the call returns before the GPU finishes; synchronise the stream
- *    before reading outputs.
+ *  - `stream` is a hipStream_t (NULL = the default stream), declared as void*
+ *    so that this header compiles as plain C99 without the HIP headers.  Work
+ *    is enqueued on it and the call returns before the GPU finishes;
+ *    synchronise the stream before reading outputs.
  *  - Argument errors are detected on the host before anything is enqueued and
  *    returned as a status; SL_ERR_HIP reports a launch failure.
  *  - Element counts are int64; n must be a multiple of SL_CHUNK.
@@ -96,9 +97,9 @@ sl_status sl_compress(const float* delta, float* ef, float beta, uint8_t* payloa
 /*
  * sl_compress_weights -- sl_compress with the pseudo-gradient formed on the fly.
  *
- * The step before compression: "Why DiLoCo Alone Isn't Enough" in [SF] defines
- * the pseudo-gradient as the difference between the pre- and post-inner-loop
- * weights.  Reading: delta[i] = theta_pre[i] - theta_post[i] (one fp32
+ * The step before compression ([SF], section "Why DiLoCo Alone Isn't Enough",
+ * which defines the pseudo-gradient from the weights on either side of the
+ * inner loop).  Reading: delta[i] = theta_pre[i] - theta_post[i] (one fp32
  * subtraction), then exactly sl_compress(delta, ef, ...), so the results are
  * bitwise those of materialising delta first; delta never reaches HBM.
  *
@@ -185,7 +186,11 @@ sl_status sl_aggregate_apply(const uint8_t* const* payloads, const float* const*
  * n_chunks number of records (0 is a no-op)
  * flags    out uint8[n_chunks], must not overlap payload or scales; flags[c] is 0
  *          for a well-formed record, else bit 0 = indices not strictly
- *          increasing, bit 1 = scale not finite, bit 2 = scale negative
+ *          increasing, bit 1 = scale not finite, bit 2 = scale negative.
+ *          One byte per record rather than a single device counter of bad
+ *          records: the caller learns which records failed and which check,
+ *          and the count is the number of non-zero flags (sl_peer_stats
+ *          returns it per peer in the same pass).
  */
 sl_status sl_validate_payload(const uint8_t* payload, const float* scales, int64_t n_chunks,
                               uint8_t* flags, void* stream);
@@ -252,7 +257,10 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
  */
 sl_status sl_host_device_pointer(const void* host_ptr, void** device_ptr);
 
-/* Human-readable name of a status code (static storage, never NULL). */
+/* Human-readable name of a status code (static storage, never NULL).  Takes an
+ * int rather than sl_status so that any stored value, including one outside
+ * the enumeration, is well defined to pass; unknown values give
+ * "unknown sl_status". */
 const char* sl_status_string(int status);
 
 #ifdef __cplusplus

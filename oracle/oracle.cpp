@@ -325,8 +325,8 @@ void orc_peer_stats(const uint8_t* payload, const float* scales, int64_t n_chunk
 
 void orc_pseudo_gradient(const float* theta_pre, const float* theta_post, int64_t n,
                          float* delta) {
-    /* [SF] "Why DiLoCo Alone Isn't Enough": the pseudo-gradient is the difference
-     * between the pre- and post-inner-loop weights; R11: pre - post. */
+    /* [SF] "Why DiLoCo Alone Isn't Enough" (pseudo-gradient from the weights on
+     * either side of the inner loop); R11 fixes the sign: pre - post. */
     for (int64_t i = 0; i < n; ++i) delta[i] = theta_pre[i] - theta_post[i];
 }
 

@@ -204,7 +204,8 @@ def test_telescoping_with_beta_one(orc):
 
 
 def test_quiet_coordinate_breaks_through(orc):
-    """A coordinate that keeps missing the cut builds up in ef until it is sent:
+    """A small persistent value below the cut accumulates in ef round after round
+    until it is selected:
     64 loud entries of magnitude 1 each round, one quiet entry of +0.01."""
     ef = np.zeros(4096, np.float32)
     rng = np.random.default_rng(3)

@@ -45,7 +45,7 @@ def _raw_compress_into(orc, delta, guard_bytes=512):
 
 
 def test_payload_size_and_ratio(orc):
-    """[SF] layout formula: 64 x 14 bits = 896 bits = 112 bytes per chunk, and the
+    """[SF] layout formula: 64 entries of (2 + 12) bits make 896 bits, 112 bytes per chunk; the
     ratio 16,384 / 112 = 146.3x.  Measured from where the oracle stops writing."""
     rng = np.random.default_rng(1)
     C = 8
