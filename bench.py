@@ -10,7 +10,13 @@ decoder-block workload) is timed separately on the same sizes, and the
 fused aggregate + update and the other entry points under "next_rows".
 Inputs are resident in HBM before timing starts.  Prints one JSON line.
 
+Besides the step, it times the same aggregate over rotating record sets whose
+total exceeds the 256 MB last-level cache ("aggregate_cold": every call reads
+its records from HBM, as a round's freshly received records are), the
+compressor's warmup calls, and the entry points of the NEXT rows.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --summarize-profile DIR   (rocprofv3 CSV output -> profiles/*.txt)
 """
 from __future__ import annotations
 
@@ -94,11 +100,22 @@ def parse():
     ap.add_argument("--cpu-sample-chunks", type=int, default=57344)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a torch copy of 1 GiB (for counter calibration)")
+    ap.add_argument("--cold-sets", type=int, default=4,
+                    help="independent 24-peer record sets the cold aggregate rotates through")
+    ap.add_argument("--workload-shapes", default="small_1m,attn_8192x8192,decoder_block,flat_16b,mlp_many_peers",
+                    help="comma-separated shapes the workloads section times")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="write profiles/*.txt from the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--profile-out", metavar="DIR", default=os.path.join(ROOT, "profiles"),
+                    help="where --summarize-profile writes (default: profiles/)")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.profile_out)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the compressor and aggregator are chunk-local, "
               "and a multi-GPU run would shard chunk ranges and all-gather the records, which "
@@ -137,6 +154,20 @@ def main():
         peer_p.append(pl)
         peer_s.append(s)
         del d
+    # Further independent record sets (peers 25, 26, ...) for the cold
+    # aggregate: 4 sets x 160 MB exceed the last-level cache, so each call's
+    # records come from HBM.
+    cold_sets = [sl.PeerSet(peer_p, peer_s)]
+    for k in range(1, max(1, args.cold_sets)):
+        cp, cs = [], []
+        for p in range(k * N_PEERS + 1, (k + 1) * N_PEERS + 1):
+            d = datagen.student_t3(n, W, p, 0, dev)
+            scratch_ef.zero_()
+            pl, s = sl.compress(d, scratch_ef, BETA)
+            cp.append(pl)
+            cs.append(s)
+            del d
+        cold_sets.append(sl.PeerSet(cp, cs))
     del scratch_ef
     torch.cuda.synchronize()
 
@@ -160,9 +191,13 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    # Warmup steps, each compress call timed, so the line shows whether the
+    # timed steps start in the steady state.
+    wevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.warmup)]
+    for k in range(args.warmup):
+        step(wevs[k])
     torch.cuda.synchronize()
+    t_warm = [e[0].elapsed_time(e[1]) for e in wevs]
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -177,6 +212,25 @@ def main():
     t_a = [e[1].elapsed_time(e[2]) for e in evs]
     span_ms = evs[0][0].elapsed_time(evs[-1][2])
     ms_per_step = span_ms / K
+
+    # The same step with the aggregate's records read from HBM: each step
+    # takes the next of the rotating record sets.
+    def step_cold(k, ev):
+        ev[0].record(stream)
+        sl.sl_compress(delta, ef, BETA, payload, scales)
+        ev[1].record(stream)
+        sl.sl_aggregate(cold_sets[k % len(cold_sets)], None, out)
+        ev[2].record(stream)
+
+    for k in range(len(cold_sets)):
+        step_cold(k, [torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for k in range(K):
+        step_cold(k, cevs[k])
+    torch.cuda.synchronize()
+    t_cc = [e[0].elapsed_time(e[1]) for e in cevs]
+    t_ac = [e[1].elapsed_time(e[2]) for e in cevs]
+    ms_per_step_cold = cevs[0][0].elapsed_time(cevs[-1][2]) / K
 
     # The outer update, outside the step: same K, one event pair per call.
     for _ in range(args.warmup):
@@ -203,6 +257,15 @@ def main():
 
     value = n / (ms_per_step * 1e-3) / 1e9
     comp = kstats(tc, BYTES_COMPRESS, t_c)
+    comp["first_timed_ms"] = round(t_c[0], 5)
+    comp["last_timed_ms"] = round(t_c[-1], 5)
+    agg_cold = kstats(avg(t_ac), BYTES_AGGREGATE, t_ac)
+    agg_cold.update({"record_sets": len(cold_sets),
+                     "record_bytes_per_set": N_PEERS * C * RECORD,
+                     "note": "each call aggregates the next of the record sets, whose total exceeds the "
+                             "256 MB last-level cache: the records come from HBM"})
+    step_cold_stats = kstats(ms_per_step_cold, BYTES_COMPRESS + BYTES_AGGREGATE)
+    step_cold_stats["compress_ms"] = round(avg(t_cc), 5)
     traffic = traffic_from_profile(n)
     result = {
         "metric": METRIC,
@@ -240,6 +303,17 @@ def main():
             "aggregate": kstats(ta, BYTES_AGGREGATE, t_a),
             "apply_mean": kstats(tm, BYTES_APPLY, t_m),
             "compress_plus_aggregate": kstats(tc + ta, BYTES_COMPRESS + BYTES_AGGREGATE),
+            "aggregate_cold": agg_cold,
+            "step_cold": step_cold_stats,
+        },
+        "warmup_trace": {
+            "steps": args.warmup,
+            "compress_ms_first": round(t_warm[0], 5) if t_warm else None,
+            "compress_ms_last": round(t_warm[-1], 5) if t_warm else None,
+            "compress_ms_max": round(max(t_warm), 5) if t_warm else None,
+            "timed_compress_ms_first": round(t_c[0], 5),
+            "timed_compress_ms_last": round(t_c[-1], 5),
+            "timed_compress_ms_max": round(max(t_c), 5),
         },
         "wall_s_timed": round(wall, 4),
         "device": device_props(torch, dev),
@@ -250,8 +324,8 @@ def main():
                                         stream, kstats)
 
     if not args.no_workloads:
-        del out
-        result["workloads"] = workloads(sl, dev)
+        del out, cold_sets
+        result["workloads"] = workloads(sl, dev, args.workload_shapes.split(","))
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n)
@@ -292,9 +366,17 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     res["compress_weights"] = kstats(t, 16 + RECORD / CHUNK)
     del post
     ef_host = torch.zeros(n, dtype=torch.float32, pin_memory=True)
-    t = timed(lambda: sl.sl_compress_host_ef(delta, ef_host, BETA, payload, scales), k=2, warm=1)
+    t = timed(lambda: sl.sl_compress_host_ef(delta, ef_host, BETA, payload, scales), k=5, warm=1)
     st = kstats(t, 4 + RECORD / CHUNK)       # HBM bytes only; ef moves over the host link
-    st["host_link_gb_per_s"] = round(8 * n / (t * 1e-3) / 1e9, 1)
+    link = 8 * n / (t * 1e-3) / 1e9          # ef read and written over the host link
+    dma = host_link_dma(torch, ef_host, delta.device, stream)
+    st["host_link_gb_per_s"] = round(link, 1)
+    st["host_link_peak_gb_per_s"] = dma["bidirectional_gb_per_s"]
+    st["host_link_frac"] = round(link / dma["bidirectional_gb_per_s"], 4)
+    st["host_link_dma"] = dma
+    st["host_link_note"] = ("peak = concurrent host-to-device and device-to-host copies of the same "
+                            "4 bytes per parameter each way, measured in this run; PCIe 5.0 x16 "
+                            "signals 64 GB/s per direction")
     res["compress_host_ef"] = st
     del ef_host
     flags = torch.empty(n // CHUNK, dtype=torch.uint8, device=delta.device)
@@ -310,6 +392,44 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     res["peer_stats_24_peers"] = kstats(t, N_PEERS * (RECORD + 1) / CHUNK)
     res["small_round_1m"] = small_round(sl, delta.device)
     return res
+
+
+def host_link_dma(torch, host_a, dev, stream, reps=3):
+    """Rates of the host link as the copy engines see it, on the bytes the
+    host-resident EF round moves: host-to-device and device-to-host copies of
+    the same size alone, then both at once on two streams (pinned memory)."""
+    nbytes = host_a.numel() * host_a.element_size()
+    host_b = torch.empty_like(host_a, pin_memory=True)
+    d_a = torch.empty(host_a.numel(), dtype=host_a.dtype, device=dev)
+    d_b = torch.empty_like(d_a)
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+
+    def run(h2d, d2h):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            s1.wait_stream(stream)
+            s2.wait_stream(stream)
+            if h2d:
+                with torch.cuda.stream(s1):
+                    d_a.copy_(host_a, non_blocking=True)
+            if d2h:
+                with torch.cuda.stream(s2):
+                    host_b.copy_(d_b, non_blocking=True)
+            stream.wait_stream(s1)
+            stream.wait_stream(s2)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return round((int(h2d) + int(d2h)) * nbytes / (best * 1e-3) / 1e9, 1)
+
+    r = {"bytes_each_way": nbytes, "h2d_gb_per_s": run(True, False), "d2h_gb_per_s": run(False, True),
+         "bidirectional_gb_per_s": run(True, True)}
+    del host_b, d_a, d_b
+    return r
 
 
 def timed_calls(torch, stream, fn, k=20, warm=3):
@@ -331,7 +451,7 @@ def timed_calls(torch, stream, fn, k=20, warm=3):
     return sum(t) / k, t
 
 
-def workloads(sl, dev, reps=10):
+def workloads(sl, dev, shapes, reps=10):
     """Compress and the 24-peer aggregate at the other workload shapes: the
     1,048,576-parameter case (cache-resident), one 8192 x 8192 projection, one
     decoder block (also the fused aggregate + update and apply_mean), and the
@@ -353,6 +473,8 @@ def workloads(sl, dev, reps=10):
     res = {}
     for name, W in (("small_1m", datagen.SMALL_1M), ("attn_8192x8192", datagen.ATTN_8192),
                     ("decoder_block", datagen.DECODER_BLOCK), ("flat_16b", datagen.FLAT_16B)):
+        if name not in shapes:
+            continue
         n = datagen.WORKLOAD_PARAMS[W]
         C = n // CHUNK
         need = 3 * 4 * n + N_PEERS * C * RECORD + (4 << 30)
@@ -392,6 +514,56 @@ def workloads(sl, dev, reps=10):
         del a, ef, out, payload, scales, pp, ps, peers
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+    if "mlp_many_peers" in shapes:
+        res["mlp_many_peers"] = many_peers(sl, dev, reps)
+    return res
+
+
+MANY_PEERS = (36, 48, 55, 64, 81, 128)
+
+
+def many_peers(sl, dev, reps):
+    """The aggregate at 8192 x 28672 with more peers than the step's 24: 36 to
+    128 distinct peers' records (240 to 850 MB, beyond the last-level cache,
+    so every call reads them from HBM), each count timed back to back."""
+    import torch
+
+    from communication_efficient_distributed_amd import datagen
+
+    W = datagen.MLP_8192x28672
+    n = datagen.WORKLOAD_PARAMS[W]
+    C = n // CHUNK
+    stream = torch.cuda.current_stream(dev)
+    ef = torch.empty(n, dtype=torch.float32, device=dev)
+    pp, ps = [], []
+    for p in range(1, max(MANY_PEERS) + 1):
+        d = datagen.student_t3(n, W, p, 0, dev)
+        ef.zero_()
+        x, y = sl.compress(d, ef, BETA)
+        pp.append(x)
+        ps.append(y)
+        del d
+    del ef
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    res = {"params": n, "chunks": C}
+    for P in MANY_PEERS:
+        peers = sl.PeerSet(pp[:P], ps[:P])
+        for _ in range(3):
+            sl.sl_aggregate(peers, None, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sl.sl_aggregate(peers, None, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps
+        bpp = 4 + P * RECORD / CHUNK
+        gbs = bpp * n / (t * 1e-3) / 1e9
+        res[str(P)] = {"ms": round(t, 5), "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "bytes_per_param": round(bpp, 4), "record_mb": round(P * C * RECORD / 1e6, 1)}
+    del pp, ps, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return res
 
 
@@ -565,6 +737,319 @@ def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
                               "aggregate_gparams_per_s": g(m1, da1),
                               "sample": f"first {S1} chunks, {dt1:.2f} s wall on 1 thread"},
             "host_cpu": host_cpu_model(), "host_cpus_visible": os.cpu_count()}
+
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries.  `python bench.py --summarize-profile DIR` turns the CSV
+# output of PROFILE_COMMANDS (run with DIR in place of <dir>) into the text
+# files under profiles/; every figure there, and the traffic figure that the
+# roofline object reads back, comes from this code.
+
+PROFILE_ARGS = "--no-cpu-baseline --copy-calibration --steps 3 --warmup 1 --workload-shapes decoder_block,mlp_many_peers"
+TRACE_ARGS = "--no-cpu-baseline"
+COUNTER_PASSES = (
+    ("fetch", "FETCH_SIZE"),
+    ("write", "WRITE_SIZE"),
+    ("sq", "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD "
+           "SQ_INSTS_VMEM_WR SQ_WAVE_CYCLES"),
+    ("occ", "VALUBusy OccupancyPercent MeanOccupancyPerCU"),
+)
+SQ_COUNTERS = COUNTER_PASSES[2][1].split()
+OCC_COUNTERS = (("VALUBusy", "% of kernel time a CU issues VALU"),
+                ("OccupancyPercent", "% of the 32 wave slots per CU"),
+                ("MeanOccupancyPerCU", "waves resident per CU"))
+PROFILE_COMMANDS = [
+    f"cd /tmp && TMPDIR=/tmp timeout -s KILL 900 rocprofv3 --pmc {ctr} --output-format csv -d <dir>/{name} "
+    f"-o {name} -- python3 <repo>/bench.py {PROFILE_ARGS} > <dir>/{name}.log"
+    for name, ctr in COUNTER_PASSES] + [
+    f"cd /tmp && TMPDIR=/tmp timeout -s KILL 900 rocprofv3 --kernel-trace --stats --output-format csv "
+    f"-d <dir>/trace -o trace -- python3 <repo>/bench.py {TRACE_ARGS} > <dir>/trace.log",
+    "python3 <repo>/bench.py --summarize-profile <dir>"]
+COPY_KERNEL = "copyBuffer"             # the runtime's device copy (the calibration copies)
+COPY_BYTES = 1 << 30                   # bench.py --copy-calibration copies exactly 1 GiB, three times
+MLP_PARAMS = 8192 * 28672
+DECODER_PARAMS = 855_638_016
+WORKLOAD_CHUNKS = {256: "1M", 16384: "8192x8192", 57344: "8192x28672", 208896: "decoder block",
+                   3906250: "16e9 span"}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(base, name, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(base, name, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {os.path.join(base, name)}")
+    return hits[0]
+
+
+def _bench_line(path):
+    """The JSON line bench.py printed in a profiled run (its steps, warmup, sets)."""
+    with open(path) as f:
+        for line in f:
+            if line.startswith("{"):
+                return json.loads(line)
+    raise ValueError(f"no bench JSON line in {path}")
+
+
+def _counter_dispatches(path):
+    """Dispatches in order, each with its kernel, total work-items and the sum of
+    every row of each counter (some counters are reported in several rows)."""
+    by = {}
+    for r in _csv_rows(path):
+        d = by.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                  "wg": int(r["Workgroup_Size"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [dict(v, dispatch=k) for k, v in sorted(by.items())]
+
+
+def _chunks_of(kernel, grid_items, wg):
+    """Chunks covered by one launch of an sl:: kernel (grids are padded to a
+    multiple of 8 workgroups, one per XCD; the run kernel sums 2 or 3 chunks per
+    wavefront)."""
+    groups = grid_items // max(wg, 1)
+    if "aggregate_run_kernel" in kernel:
+        cpw = 2 if "<9, 2>" in kernel else 3
+        cands = [c for c in WORKLOAD_CHUNKS if ((c + cpw - 1) // cpw + 7) // 8 * 8 == groups]
+    else:
+        cands = [c for c in WORKLOAD_CHUNKS if (c + 7) // 8 * 8 == groups or c == groups]
+    return cands[0] if cands else groups
+
+
+def _sl_key(kernel):
+    """Short kernel name: the function and its template arguments."""
+    k = kernel.replace("sl::(anonymous namespace)::", "").replace("void ", "")
+    return k.split("(")[0].strip()
+
+
+def _label_mlp(dispatches, line):
+    """Label the sl:: dispatches at the 8192 x 28672 shape by the role they play
+    in bench.py's run, from its fixed call order."""
+    W, K, S = line["warmup"], line["steps"], line["kernels"]["aggregate_cold"]["record_sets"]
+    peers = line["config"]["peers"]
+    C = MLP_PARAMS // CHUNK
+    seen = {}
+    out = []
+    for d in dispatches:
+        name = _sl_key(d["kernel"])
+        if not name.startswith(("compress_kernel", "aggregate", "apply_mean")):
+            continue
+        chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
+        key = (name, chunks)
+        i = seen.get(key, 0)
+        seen[key] = i + 1
+        label = None
+        if chunks == C:
+            if name == "compress_kernel<false>":
+                label = "compress" if i < peers * S + W + K + S + K else "compress_host_ef"
+            elif name.startswith("aggregate_kernel<") and name.endswith("false>"):
+                label = "aggregate" if i < W + K else ("aggregate_cold" if i < W + K + S + K else None)
+            elif name == "apply_mean_kernel":
+                label = "apply_mean"
+            elif name.startswith("aggregate_apply4_kernel"):
+                label = "aggregate_apply"
+            elif name == "compress_kernel<true>":
+                label = "compress_weights"
+        if label:
+            out.append((label, d))
+    return out
+
+
+def _calibration(dispatches, counter):
+    vals = [d[counter] for d in dispatches if COPY_KERNEL in d["kernel"]]
+    if len(vals) < 3 or len(vals) % 3:
+        raise ValueError(f"expected three calibration copies of {COPY_BYTES} bytes, found {len(vals)} dispatches")
+    per = len(vals) // 3                        # dispatches per copy
+    kib = sum(vals[-3 * per:]) / 3              # the three copies' KiB each
+    return kib, COPY_BYTES / (kib * 1024)
+
+
+def _header(title, extra=()):
+    lines = [f"# rocprofv3 counters: {title}", "# commands (run on the GPU box; <dir> is the summary's input):"]
+    lines += [f"#   {c}" for c in PROFILE_COMMANDS]
+    lines += [f"# {e}" for e in extra]
+    return lines
+
+
+def _kernel_sources(which):
+    csrc = [os.path.join(CSRC, f) for f in ("wave.h", "residency.h", "internal.h")]
+    inc = [os.path.join(ROOT, "include", "sparseloco.h")]
+    if which == "compress":
+        return [os.path.join(CSRC, "compress.hip")] + csrc + inc
+    return [os.path.join(CSRC, "aggregate.hip"), os.path.join(CSRC, "record.h")] + csrc + inc
+
+
+def _counter_block(ds, by_pass, algo_read, algo_write, f_fac, w_fac, per_chunk):
+    """Averages of every counter over the given dispatches (matched by id in each
+    pass), with traffic scaled by the copy calibration."""
+    ids = [d["dispatch"] for d in ds]
+
+    def mean(pass_name, ctr):
+        rows = [by_pass[pass_name][i] for i in ids if i in by_pass[pass_name]]
+        if not rows or ctr not in rows[0]:
+            return None
+        return sum(r[ctr] for r in rows) / len(rows)
+
+    fk, wk = mean("fetch", "FETCH_SIZE"), mean("write", "WRITE_SIZE")
+    rb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
+    lines = [f"dispatches_sampled: {len(ids)}",
+             f"FETCH_SIZE_KiB_per_dispatch: {fk:.1f}",
+             f"WRITE_SIZE_KiB_per_dispatch: {wk:.1f}",
+             f"hbm_read_bytes_per_launch: {rb:.4g}   (algorithmic {algo_read:.4g}, ratio {rb / algo_read:.3f})",
+             f"hbm_write_bytes_per_launch: {wb:.4g}   (algorithmic {algo_write:.4g}, ratio {wb / algo_write:.3f})",
+             ""]
+    for c, what in OCC_COUNTERS:
+        v = mean("occ", c)
+        if v is not None:
+            lines.append(f"{c:<24}{v:>12.2f}   ({what})")
+    lines.append("")
+    for c in SQ_COUNTERS:
+        v = mean("sq", c)
+        if v is not None:
+            lines.append(f"{c:<24}{v:>13.4g}   per 4096-chunk {v / per_chunk:>10.2f}")
+    return lines, rb + wb
+
+
+def summarize_profile(base, outdir):
+    """Write the counter and kernel-trace summaries for the run under `base`."""
+    by_pass, lines_of = {}, {}
+    for name, _ in COUNTER_PASSES:
+        ds = _counter_dispatches(_find(base, name, "counter_collection.csv"))
+        by_pass[name] = {d["dispatch"]: d for d in ds}
+        lines_of[name] = ds
+    line = _bench_line(os.path.join(base, "fetch.log"))
+    f_kib, f_fac = _calibration(lines_of["fetch"], "FETCH_SIZE")
+    w_kib, w_fac = _calibration(lines_of["write"], "WRITE_SIZE")
+    cal = [f"Calibration: bench.py --copy-calibration runs three device copies of exactly 1 GiB; FETCH_SIZE "
+           f"reads {f_kib:.1f} KiB per copy (factor {f_fac:.4f}), WRITE_SIZE {w_kib:.1f} KiB (factor {w_fac:.4f})."]
+    n, C = MLP_PARAMS, MLP_PARAMS // CHUNK
+    P = line["config"]["peers"]
+    rec = P * RECORD / CHUNK
+    labelled = _label_mlp(lines_of["fetch"], line)
+    roles = {
+        "compress": ("compress_kernel<false>", 8.0, 4.0 + RECORD / CHUNK, "compress"),
+        "compress_weights": ("compress_kernel<true>", 12.0, 4.0 + RECORD / CHUNK, "compress"),
+        "aggregate": ("aggregate_kernel, records cache-resident (the same 24 peers every call)", rec, 4.0, "aggregate"),
+        "aggregate_cold": ("aggregate_kernel, records from HBM (four rotating record sets)", rec, 4.0, "aggregate"),
+        "apply_mean": ("apply_mean_kernel", 8.0, 4.0, "aggregate"),
+        "aggregate_apply": ("aggregate_apply4_kernel", 4.0 + rec, 4.0, "aggregate"),
+    }
+    written = []
+    files = {"compress": "compress_mlp_8192x28672_counters.txt",
+             "compress_weights": "compress_weights_mlp_8192x28672_counters.txt",
+             "aggregate": "aggregate_mlp_8192x28672_counters.txt",
+             "apply_mean": "apply_mean_mlp_8192x28672_counters.txt",
+             "aggregate_apply": "aggregate_apply_mlp_8192x28672_counters.txt"}
+    sections = {}
+    for role, (title, rd, wr, src) in roles.items():
+        ds = [d for lab, d in labelled if lab == role]
+        if not ds:
+            continue
+        body, total = _counter_block(ds, by_pass, rd * n, wr * n, f_fac, w_fac, C)
+        head = [f"[{title}]", f"{src}_code_sha256_16: {code_digest(_kernel_sources(src))}   "
+                f"({src}.hip and the headers it includes, comments and whitespace removed)",
+                f"params_per_launch: {n}"] + body
+        if role == "compress":
+            head.insert(3, f"compress_hbm_bytes_per_launch: {total:.6g}")
+        sections[role] = head
+    for role, fname in files.items():
+        if role not in sections:
+            continue
+        body = sections[role] + ([""] + sections["aggregate_cold"] if role == "aggregate" and
+                                 "aggregate_cold" in sections else [])
+        lines = _header(f"{roles[role][0].split(',')[0]}, 8192 x 28672 fp32 ({n:,} params), {P} peers", cal) + [""] + body
+        path = os.path.join(outdir, fname)
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(path)
+    # Run kernels: the decoder block (24 peers) and the many-peer aggregate.
+    run_sections = []
+    for d in lines_of["fetch"]:
+        name = _sl_key(d["kernel"])
+        if not name.startswith("aggregate_run_kernel") and not (name.startswith("aggregate_kernel<")
+                                                                  and name.endswith("false>")):
+            continue
+        chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
+        if chunks == 208896 and name.startswith("aggregate_run_kernel"):
+            run_sections.append(("decoder block, 24 peers", name, d, DECODER_PARAMS, 24))
+    many = line.get("workloads", {}).get("mlp_many_peers", {})
+    counts = [int(k) for k in many if k.isdigit()]
+    if counts:
+        # the many-peer section calls sl_aggregate 3 + reps times per count, in MANY_PEERS order
+        ds = [d for d in lines_of["fetch"] if _chunks_of(d["kernel"], d["grid"], d["wg"]) == C and
+              _sl_key(d["kernel"]).startswith(("aggregate_run_kernel", "aggregate_kernel<")) and
+              _sl_key(d["kernel"]).endswith(("false>", "3>", "2>"))]
+        taken = sum(1 for lab, _ in labelled if lab in ("aggregate", "aggregate_cold"))
+        ds = ds[taken:]
+        per = len(ds) // len(counts) if counts else 0
+        for j, Pm in enumerate(sorted(counts)):
+            for d in ds[j * per:(j + 1) * per][3:]:
+                run_sections.append((f"8192 x 28672, {Pm} peers", _sl_key(d["kernel"]), d, n, Pm))
+    if run_sections:
+        lines = _header("aggregate kernels with records beyond the last-level cache", cal)
+        lines += [f"aggregate_code_sha256_16: {code_digest(_kernel_sources('aggregate'))}   "
+                  "(aggregate.hip and the headers it includes, comments and whitespace removed)"]
+        groups = {}
+        for label, name, d, params, Pm in run_sections:
+            groups.setdefault((label, name, params, Pm), []).append(d)
+        for (label, name, params, Pm), ds in groups.items():
+            body, _ = _counter_block(ds, by_pass, Pm * RECORD / CHUNK * params, 4.0 * params, f_fac, w_fac,
+                                     params // CHUNK)
+            lines += ["", f"[{label}: {name}]"] + body
+        path = os.path.join(outdir, "aggregate_beyond_cache_counters.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(path)
+    trace = os.path.join(base, "trace")
+    if os.path.isdir(trace):
+        written.append(summarize_trace(base, outdir))
+    for p in written:
+        print(p)
+    return written
+
+
+def summarize_trace(base, outdir):
+    """Per-kernel durations of every sl:: dispatch in the kernel-trace run,
+    grouped by kernel and workload shape, with the bench line of the same run."""
+    rows = _csv_rows(_find(base, "trace", "kernel_trace.csv"))
+    line = _bench_line(os.path.join(base, "trace.log"))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ds = [{"kernel": r["Kernel_Name"], "grid": int(r["Grid_Size_X"]), "wg": int(r["Workgroup_Size_X"]),
+           "peers": int(r["Grid_Size_Y"]), "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3}
+          for r in rows if "sl::" in r["Kernel_Name"]]
+    role = {id(d): lab for lab, d in _label_mlp(ds, line)}
+    suffix = {"aggregate": ", records cached", "aggregate_cold": ", records from HBM",
+              "compress_host_ef": ", ef in host memory"}
+    groups = {}
+    for d in ds:
+        chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
+        label = f"{_sl_key(d['kernel'])} [{WORKLOAD_CHUNKS.get(chunks, f'{chunks} chunks')}" \
+                f"{suffix.get(role.get(id(d)), '')}]"
+        if d["peers"] > 1:
+            label += f" x{d['peers']} peers"
+        groups.setdefault(label, []).append(d["us"])
+    lines = [f"# rocprofv3 kernel trace of the default bench run (every sl:: dispatch, all shapes)",
+             "# command:", f"#   {PROFILE_COMMANDS[len(COUNTER_PASSES)]}", f"#   {PROFILE_COMMANDS[-1]}",
+             "# Durations are per dispatch from the kernel trace, all dispatches of the run (setup, warmup,",
+             "# timed).  The bench line's own HIP-event means for the same run follow the table.", "",
+             f"{'kernel [shape]':<58}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}"]
+    for label, ds in groups.items():
+        lines.append(f"{label:<58}{len(ds):>7}{sum(ds) / len(ds):>11.2f}{min(ds):>11.2f}{max(ds):>11.2f}")
+    k = line["kernels"]
+    lines += ["", "# bench.py line of the same run (HIP events on the launch stream, timed steps only):",
+              f"#   value {line['value']} Gparams/s, ms_per_step {line['ms_per_step']}, compress ms "
+              f"{k['compress']['ms']}, aggregate ms {k['aggregate']['ms']}, aggregate_cold ms "
+              f"{k['aggregate_cold']['ms']}, apply_mean ms {k['apply_mean']['ms']}",
+              f"#   roofline: {json.dumps(line['roofline'])}"]
+    path = os.path.join(outdir, "sl_kernels_mlp_8192x28672_kernel_trace.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
 
 
 if __name__ == "__main__":
