@@ -106,9 +106,16 @@ def parse():
                     help="comma-separated shapes the workloads section times")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="write profiles/*.txt from the rocprofv3 CSV output under DIR and exit")
+    ap.add_argument("--progress", action="store_true",
+                    help="print a line to stderr as each stage of the run ends")
     ap.add_argument("--profile-out", metavar="DIR", default=os.path.join(ROOT, "profiles"),
                     help="where --summarize-profile writes (default: profiles/)")
     return ap.parse_args()
+
+
+def stage(args, what):
+    if args.progress:
+        print(f"[bench] {time.strftime('%H:%M:%S')} {what}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -131,6 +138,15 @@ def main():
     sl.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # Three device copies of exactly 1 GiB, before any other kernel of the
+        # run, so that a counter summary finds them as the run's first dispatches.
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     W = datagen.MLP_8192x28672
     n = datagen.WORKLOAD_PARAMS[W]
     C = n // CHUNK
@@ -170,14 +186,7 @@ def main():
         cold_sets.append(sl.PeerSet(cp, cs))
     del scratch_ef
     torch.cuda.synchronize()
-
-    if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    stage(args, f"setup: {len(cold_sets)} record sets of {N_PEERS} peers")
 
     stream = torch.cuda.current_stream(dev)
 
@@ -198,6 +207,7 @@ def main():
         step(wevs[k])
     torch.cuda.synchronize()
     t_warm = [e[0].elapsed_time(e[1]) for e in wevs]
+    stage(args, f"{args.warmup} warmup steps")
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -231,6 +241,7 @@ def main():
     t_cc = [e[0].elapsed_time(e[1]) for e in cevs]
     t_ac = [e[1].elapsed_time(e[2]) for e in cevs]
     ms_per_step_cold = cevs[0][0].elapsed_time(cevs[-1][2]) / K
+    stage(args, f"{K} timed steps, cached and cold records")
 
     # The outer update, outside the step: same K, one event pair per call.
     for _ in range(args.warmup):
@@ -322,13 +333,15 @@ def main():
     if not args.no_next_rows:
         result["next_rows"] = next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n,
                                         stream, kstats)
+        stage(args, "next rows")
 
     if not args.no_workloads:
         del out, cold_sets
-        result["workloads"] = workloads(sl, dev, args.workload_shapes.split(","))
+        result["workloads"] = workloads(sl, dev, args.workload_shapes.split(","), lambda w: stage(args, w))
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n)
+        stage(args, "cpu baseline")
 
     print(json.dumps(result), flush=True)
 
@@ -451,7 +464,7 @@ def timed_calls(torch, stream, fn, k=20, warm=3):
     return sum(t) / k, t
 
 
-def workloads(sl, dev, shapes, reps=10):
+def workloads(sl, dev, shapes, done=lambda what: None, reps=10):
     """Compress and the 24-peer aggregate at the other workload shapes: the
     1,048,576-parameter case (cache-resident), one 8192 x 8192 projection, one
     decoder block (also the fused aggregate + update and apply_mean), and the
@@ -511,11 +524,13 @@ def workloads(sl, dev, shapes, reps=10):
             t, ts = timed_calls(torch, stream, lambda: sl.sl_apply_mean(theta, out, N_PEERS), k=reps)
             r["apply_mean"] = st(n, t, BYTES_APPLY, ts)
         res[name] = r
+        done(f"workload {name}")
         del a, ef, out, payload, scales, pp, ps, peers
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     if "mlp_many_peers" in shapes:
         res["mlp_many_peers"] = many_peers(sl, dev, reps)
+        done("workload mlp_many_peers")
     return res
 
 
@@ -746,8 +761,9 @@ def cpu_baseline(args, delta, ef0_host, peer_p, peer_s, theta, n):
 # files under profiles/; every figure there, and the traffic figure that the
 # roofline object reads back, comes from this code.
 
-PROFILE_ARGS = "--no-cpu-baseline --copy-calibration --steps 3 --warmup 1 --workload-shapes decoder_block,mlp_many_peers"
-TRACE_ARGS = "--no-cpu-baseline"
+PROFILE_ARGS = ("--no-cpu-baseline --copy-calibration --steps 3 --warmup 1 --progress "
+                "--workload-shapes decoder_block,mlp_many_peers")
+TRACE_ARGS = "--no-cpu-baseline --progress"
 COUNTER_PASSES = (
     ("fetch", "FETCH_SIZE"),
     ("write", "WRITE_SIZE"),
@@ -832,23 +848,31 @@ def _label_mlp(dispatches, line):
     in bench.py's run, from its fixed call order."""
     W, K, S = line["warmup"], line["steps"], line["kernels"]["aggregate_cold"]["record_sets"]
     peers = line["config"]["peers"]
+    n_step = peers * S + W + K + S + K       # setup, warmup, timed, cold-step compressions
+    n_host = 6 if "next_rows" in line else 0  # then the host-resident EF row: 1 warmup + 5 timed
     C = MLP_PARAMS // CHUNK
     seen = {}
     out = []
+    step_agg = None         # the step's aggregate kernel: the first one-chunk aggregate at this shape
     for d in dispatches:
         name = _sl_key(d["kernel"])
         if not name.startswith(("compress_kernel", "aggregate", "apply_mean")):
             continue
         chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
+        if step_agg is None and chunks == C and name.startswith("aggregate_kernel<") and name.endswith("false>"):
+            step_agg = name
         key = (name, chunks)
         i = seen.get(key, 0)
         seen[key] = i + 1
         label = None
         if chunks == C:
             if name == "compress_kernel<false>":
-                label = "compress" if i < peers * S + W + K + S + K else "compress_host_ef"
-            elif name.startswith("aggregate_kernel<") and name.endswith("false>"):
-                label = "aggregate" if i < W + K else ("aggregate_cold" if i < W + K + S + K else None)
+                timed = peers * S + W <= i < peers * S + W + K
+                label = "compress_host_ef" if n_step <= i < n_step + n_host else (
+                    "compress_timed" if timed else "compress")
+            elif name == step_agg:
+                label = ("aggregate_timed" if W <= i < W + K else "aggregate") if i < W + K else (
+                    "aggregate_cold" if i < W + K + S + K else None)
             elif name == "apply_mean_kernel":
                 label = "apply_mean"
             elif name.startswith("aggregate_apply4_kernel"):
@@ -861,11 +885,18 @@ def _label_mlp(dispatches, line):
 
 
 def _calibration(dispatches, counter):
-    vals = [d[counter] for d in dispatches if COPY_KERNEL in d["kernel"]]
+    """The run's leading copy dispatches are the three calibration copies
+    (bench.py makes them before any other kernel): KiB per copy and the factor
+    that turns the counter into bytes."""
+    vals = []
+    for d in dispatches:
+        if COPY_KERNEL not in d["kernel"]:
+            break
+        vals.append(d[counter])
     if len(vals) < 3 or len(vals) % 3:
-        raise ValueError(f"expected three calibration copies of {COPY_BYTES} bytes, found {len(vals)} dispatches")
-    per = len(vals) // 3                        # dispatches per copy
-    kib = sum(vals[-3 * per:]) / 3              # the three copies' KiB each
+        raise ValueError(f"expected the run to start with three copies of {COPY_BYTES} bytes, "
+                         f"found {len(vals)} leading copy dispatches")
+    kib = sum(vals) / 3
     return kib, COPY_BYTES / (kib * 1024)
 
 
@@ -916,7 +947,22 @@ def _counter_block(ds, by_pass, algo_read, algo_write, f_fac, w_fac, per_chunk):
 
 
 def summarize_profile(base, outdir):
-    """Write the counter and kernel-trace summaries for the run under `base`."""
+    """Write the counter summaries (if the four counter passes are under
+    `base`) and the kernel-trace summary (if the trace run is)."""
+    written = []
+    if os.path.isdir(os.path.join(base, COUNTER_PASSES[0][0])):
+        written += summarize_counters(base, outdir)
+    if os.path.isdir(os.path.join(base, "trace")):
+        written.append(summarize_trace(base, outdir))
+    if not written:
+        raise FileNotFoundError(f"no rocprofv3 output under {base}")
+    for p in written:
+        print(p)
+    return written
+
+
+def summarize_counters(base, outdir):
+    """Counter summaries of the run under `base` (the four passes)."""
     by_pass, lines_of = {}, {}
     for name, _ in COUNTER_PASSES:
         ds = _counter_dispatches(_find(base, name, "counter_collection.csv"))
@@ -930,7 +976,7 @@ def summarize_profile(base, outdir):
     n, C = MLP_PARAMS, MLP_PARAMS // CHUNK
     P = line["config"]["peers"]
     rec = P * RECORD / CHUNK
-    labelled = _label_mlp(lines_of["fetch"], line)
+    labelled = [(lab.replace("_timed", ""), d) for lab, d in _label_mlp(lines_of["fetch"], line)]
     roles = {
         "compress": ("compress_kernel<false>", 8.0, 4.0 + RECORD / CHUNK, "compress"),
         "compress_weights": ("compress_kernel<true>", 12.0, 4.0 + RECORD / CHUNK, "compress"),
@@ -1005,11 +1051,6 @@ def summarize_profile(base, outdir):
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
         written.append(path)
-    trace = os.path.join(base, "trace")
-    if os.path.isdir(trace):
-        written.append(summarize_trace(base, outdir))
-    for p in written:
-        print(p)
     return written
 
 
@@ -1025,18 +1066,30 @@ def summarize_trace(base, outdir):
     role = {id(d): lab for lab, d in _label_mlp(ds, line)}
     suffix = {"aggregate": ", records cached", "aggregate_cold": ", records from HBM",
               "compress_host_ef": ", ef in host memory"}
+    timed_of = {"compress_timed": "compress_kernel<false> [8192x28672, timed steps only]",
+                "aggregate_timed": "step aggregate [8192x28672, records cached, timed steps only]"}
     groups = {}
     for d in ds:
-        chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
-        label = f"{_sl_key(d['kernel'])} [{WORKLOAD_CHUNKS.get(chunks, f'{chunks} chunks')}" \
-                f"{suffix.get(role.get(id(d)), '')}]"
-        if d["peers"] > 1:
-            label += f" x{d['peers']} peers"
+        name = _sl_key(d["kernel"])
+        if name.startswith(("validate_kernel", "stats_kernel", "clear_stats_kernel")):
+            # one lane per record (validate) or a fixed grid per peer (statistics): label by grid
+            label = f"{name} [grid {d['grid']} x {d['peers']}]"
+        else:
+            chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
+            lab = role.get(id(d), "").replace("_timed", "")
+            label = f"{name} [{WORKLOAD_CHUNKS.get(chunks, f'{chunks} chunks')}{suffix.get(lab, '')}]"
+            if d["peers"] > 1:
+                label += f" x{d['peers']} peers"
+        lab = role.get(id(d))
+        if lab in timed_of:
+            groups.setdefault(timed_of[lab], []).append(d["us"])
+            label = label.replace(", timed", "")
         groups.setdefault(label, []).append(d["us"])
     lines = [f"# rocprofv3 kernel trace of the default bench run (every sl:: dispatch, all shapes)",
              "# command:", f"#   {PROFILE_COMMANDS[len(COUNTER_PASSES)]}", f"#   {PROFILE_COMMANDS[-1]}",
              "# Durations are per dispatch from the kernel trace, all dispatches of the run (setup, warmup,",
-             "# timed).  The bench line's own HIP-event means for the same run follow the table.", "",
+             "# timed).  The bench line's own HIP-event means for the same run follow the table.",
+             "# validate/stats rows: grid = lanes along x (validate: one per record) x peers.", "",
              f"{'kernel [shape]':<58}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}"]
     for label, ds in groups.items():
         lines.append(f"{label:<58}{len(ds):>7}{sum(ds) / len(ds):>11.2f}{min(ds):>11.2f}{max(ds):>11.2f}")

@@ -3,7 +3,8 @@
 The fixture mimics the CSV layout rocprofv3 writes for the four counter passes
 and the kernel trace: a bench run with 1 warmup step, 3 timed steps and 4
 record sets at 8192 x 28672, three 1 GiB calibration copies split into four
-dispatches each, and some counters reported in several rows per dispatch.  The
+dispatches each at the start (later copies of the data generator are not
+calibration), and some counters reported in several rows per dispatch.  The
 counter values are chosen so that every expected figure is known in closed
 form: the copy's FETCH_SIZE reads half its bytes (calibration factor 2), and
 each kernel's calibrated traffic equals its algorithmic bytes times a known
@@ -37,27 +38,34 @@ COMPRESS = "void sl::(anonymous namespace)::compress_kernel<false>(float const*,
            "unsigned char*, float*, long)"
 AGG = "void sl::(anonymous namespace)::aggregate_kernel<3, false>(sl::PeerTable, int, float*, long, long, float)"
 MEAN = "sl::(anonymous namespace)::apply_mean_kernel(float*, float const*, float, long)"
+RUN63 = "void sl::(anonymous namespace)::aggregate_run_kernel<6, 3>(sl::PeerTable, int, float*, long, long)"
+AGG15 = "void sl::(anonymous namespace)::aggregate_kernel<15, false>(sl::PeerTable, int, float*, long, long, float)"
+RUN_ITEMS = ((C + 2) // 3 + 7) // 8 * 8 * 64
 COPY = "__amd_rocclr_copyBuffer"
 TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >(int, at::native::FillFunctor<float>, std::array<char*, 2ul>)"
 
 # (kernel, work-items, workgroup size, KiB read, KiB written, duration us)
 AGG_ITEMS = (C + 7) // 8 * 8 * 64
 SEQUENCE = (
-    [(TORCH, 1 << 20, 256, 10.0, 20.0, 5.0)]
+    [(COPY, 1 << 20, 512, 131072.0, 262144.0, 100.0)] * 12
+    + [(TORCH, 1 << 20, 256, 10.0, 20.0, 5.0), (COPY, 1 << 16, 512, 500.0, 1000.0, 5.0)]
     + [(COMPRESS, C * 256, 256, 8 * N / 2048, (4 + REC) * N / 1024, 450.0)] * (P * S)
-    + [(COPY, 1 << 20, 512, 131072.0, 262144.0, 100.0)] * 12
     + [(COMPRESS, C * 256, 256, 8 * N / 2048 * 1.01, (4 + REC) * N / 1024, 449.0)] * (W + K)
     + [(AGG, AGG_ITEMS, 64, P * REC * N / 2048, 4 * N / 1024, 152.0)] * (W + K)
     + [(COMPRESS, C * 256, 256, 8 * N / 2048, (4 + REC) * N / 1024, 451.0), (AGG, AGG_ITEMS, 64,
                                                                             P * REC * N / 2048, 4 * N / 1024,
                                                                             220.0)] * (S + K)
     + [(MEAN, C * 256, 256, 8 * N / 2048, 4 * N / 1024, 430.0)] * (W + K)
+    # the many-peer section: 36 peers (three chunks per wavefront), then 128 (one), 3 + 2 calls each
+    + [(RUN63, RUN_ITEMS, 64, 36 * REC * N / 2048, 4 * N / 1024, 240.0)] * 5
+    + [(AGG15, AGG_ITEMS, 64, 128 * REC * N / 2048, 4 * N / 1024, 560.0)] * 5
 )
 
 
 def bench_line():
     return {"metric": bench.METRIC, "value": 350.0, "steps": K, "warmup": W, "ms_per_step": 0.67,
             "config": {"peers": P}, "roofline": {"bound": "hbm", "frac": 0.79},
+            "workloads": {"mlp_many_peers": {"params": N, "chunks": C, "36": {"ms": 0.24}, "128": {"ms": 0.56}}},
             "kernels": {"compress": {"ms": 0.45}, "aggregate": {"ms": 0.152},
                         "aggregate_cold": {"ms": 0.22, "record_sets": S}, "apply_mean": {"ms": 0.43}}}
 
@@ -129,6 +137,15 @@ def test_aggregate_summary_separates_cache_resident_and_cold_calls(summary):
     assert (out / "apply_mean_mlp_8192x28672_counters.txt").exists()
 
 
+def test_many_peer_sections_take_the_timed_calls_of_each_count(summary):
+    out, _ = summary
+    txt = (out / "aggregate_beyond_cache_counters.txt").read_text()
+    for label in ("[8192 x 28672, 36 peers: aggregate_run_kernel<6, 3>]",
+                  "[8192 x 28672, 128 peers: aggregate_kernel<15, false>]"):
+        block = txt.split(label)[1].split("\n[")[0]
+        assert "dispatches_sampled: 2" in block and "ratio 1.000" in block
+
+
 def test_headers_name_commands_that_run_committed_files_only(summary):
     out, files = summary
     for path in files:
@@ -147,6 +164,8 @@ def test_trace_summary_groups_dispatches_by_kernel_and_shape(summary):
     assert row("aggregate_kernel<3, false> [8192x28672, records from HBM]") == (S + K, 220.0)
     calls, avg = row("compress_kernel<false> [8192x28672]")
     assert calls == P * S + W + K + S + K
+    assert row("compress_kernel<false> [8192x28672, timed steps only]") == (K, 449.0)
+    assert row("step aggregate [8192x28672, records cached, timed steps only]") == (K, 152.0)
 
 
 def test_command_line_entry_point(tmp_path):
