@@ -157,34 +157,73 @@ template <int NGMAX>
 __device__ __forceinline__ void load_records(const PeerTable& peers, int32_t n_peers, int64_t chunk, int lane,
                                              ChunkRecords<NGMAX>& cr) {
     constexpr int kMaxPeers = kPeersPerLoad * NGMAX;
+    static_assert(kMaxPeers <= SL_MAX_PEERS + kPeersPerLoad, "peer index range");
     const int rp = lane / kQuads;
     const int rq = lane - kQuads * rp;
     const size_t off = (size_t)chunk * SL_PAYLOAD_BYTES + 16 * (size_t)rq;
 
-    const uint8_t* src[NGMAX];
-#pragma unroll
-    for (int g = 0; g < NGMAX; ++g) src[g] = peers.payload[0];
-#pragma unroll
-    for (int p = 1; p < kMaxPeers; ++p) {
-        if (p < n_peers) {
-            const uint8_t* pp = peers.payload[p];
-            if (rp == p % kPeersPerLoad) src[p / kPeersPerLoad] = pp;
-        }
-    }
-#pragma unroll
-    for (int g = 0; g < NGMAX; ++g) cr.r[g] = load_record16(src[g] + off);
+    // Group by group: the nine peers' pointers (scalar registers, from the
+    // kernel arguments) are used right where they are loaded, and the
+    // scheduling barrier keeps the next group's from being hoisted above this
+    // group's loads.  With every peer's pointers live at once the 9 x NGMAX
+    // pairs overflowed the scalar registers and spilled to vector lanes.
 #pragma unroll
     for (int g = 0; g < NGMAX; ++g) {
+        const uint8_t* src = peers.payload[0];
         const float* ssrc = peers.scales[0];
 #pragma unroll
         for (int q = 0; q < kPeersPerLoad; ++q) {
             const int p = kPeersPerLoad * g + q;
-            if (p < n_peers) {
-                const float* sp = peers.scales[p];
-                if (lane == q) ssrc = sp;
+            if (p >= 1 && p < SL_MAX_PEERS && p < n_peers) {
+                if (rp == q) src = peers.payload[p];
+                if (lane == q) ssrc = peers.scales[p];
             }
         }
+        cr.r[g] = load_record16(src + off);
         cr.sv[g] = ssrc[chunk];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// A lane's record and scale pointers for each group of nine peers, selected
+// once (the run kernel loads several chunks' records from the same peers):
+// lane 7 q + i reads bytes [16 i, 16 i + 16) of peer 9 g + q's records, lane
+// q < 9 reads peer 9 g + q's scales; other lanes read peer 0's.
+template <int NGMAX>
+struct LanePeers {
+    const uint8_t* rec[NGMAX];
+    const float* sc[NGMAX];
+};
+
+template <int NGMAX>
+__device__ __forceinline__ void lane_peers(const PeerTable& peers, int32_t n_peers, int lane, LanePeers<NGMAX>& lp) {
+    const int rp = lane / kQuads;
+    const int rq = lane - kQuads * rp;
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) {
+        const uint8_t* src = peers.payload[0];
+        const float* ssrc = peers.scales[0];
+#pragma unroll
+        for (int q = 0; q < kPeersPerLoad; ++q) {
+            const int p = kPeersPerLoad * g + q;
+            if (p >= 1 && p < SL_MAX_PEERS && p < n_peers) {
+                if (rp == q) src = peers.payload[p];
+                if (lane == q) ssrc = peers.scales[p];
+            }
+        }
+        lp.rec[g] = src + 16 * rq;
+        lp.sc[g] = ssrc;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int NGMAX>
+__device__ __forceinline__ void load_records_at(const LanePeers<NGMAX>& lp, int64_t chunk, ChunkRecords<NGMAX>& cr) {
+    typedef const __attribute__((address_space(1))) float gfloat;
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) {
+        cr.r[g] = load_record16(lp.rec[g] + (size_t)chunk * SL_PAYLOAD_BYTES);
+        cr.sv[g] = *(gfloat*)(lp.sc[g] + chunk);
     }
 }
 
@@ -288,8 +327,10 @@ __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, i
     if (c0 >= n_chunks) return;
     const int64_t count = n_chunks - c0 < CPW ? n_chunks - c0 : CPW;  // the same in every lane
     ChunkRecords<NGMAX> cr[CPW];
+    LanePeers<NGMAX> lp;
+    lane_peers<NGMAX>(peers, n_peers, lane, lp);
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) load_records<NGMAX>(peers, n_peers, i < count ? c0 + i : c0, lane, cr[i]);
+    for (int i = 0; i < CPW; ++i) load_records_at<NGMAX>(lp, i < count ? c0 + i : c0, cr[i]);
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         if (i < count) {
