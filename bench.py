@@ -1071,7 +1071,7 @@ def summarize_trace(base, outdir):
     groups = {}
     for d in ds:
         name = _sl_key(d["kernel"])
-        if name.startswith(("validate_kernel", "stats_kernel", "clear_stats_kernel")):
+        if name.startswith(("validate_kernel", "stats_kernel")):
             # one lane per record (validate) or a fixed grid per peer (statistics): label by grid
             label = f"{name} [grid {d['grid']} x {d['peers']}]"
         else:

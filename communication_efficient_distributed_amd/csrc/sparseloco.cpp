@@ -1,10 +1,12 @@
 // sparseloco.cpp -- the C ABI of libsparseloco.so (declared in
 // include/sparseloco.h): host-side argument checks and kernel launches.  No
-// allocation, no state, no synchronisation.
+// synchronisation; the one allocation is sl_peer_stats's scratch (below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <cmath>
+#include <map>
+#include <mutex>
 
 #include "internal.h"
 #include "sparseloco.h"
@@ -21,6 +23,38 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 sl_status from_hip(hipError_t e) { return e == hipSuccess ? SL_OK : SL_ERR_HIP; }
+
+// sl_peer_stats's scratch: one buffer per device, allocated and zeroed by the
+// first call on the device and kept until the process ends.  That first call
+// must not be made while its stream is being captured into a graph (it gets
+// SL_ERR_HIP then); later calls allocate nothing and can be captured.
+sl_status stats_scratch(void* stream, void** out) {
+    static std::mutex mu;
+    static std::map<int, void*> buffers;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SL_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = buffers.find(dev);
+    if (it != buffers.end()) {
+        *out = it->second;
+        return SL_OK;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return SL_ERR_HIP;
+    void* p = nullptr;
+    const size_t bytes = sl::peer_stats_scratch_bytes();
+    if (hipMalloc(&p, bytes) != hipSuccess) return SL_ERR_HIP;
+    // Zeroed before the first statistics kernel, which runs later on the same
+    // stream.
+    if (hipMemsetAsync(p, 0, bytes, s) != hipSuccess) {
+        (void)hipFree(p);
+        return SL_ERR_HIP;
+    }
+    buffers[dev] = p;
+    *out = p;
+    return SL_OK;
+}
 
 }  // namespace
 
@@ -146,7 +180,10 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
             table.scales[p] = scales[p];
         }
     }
-    return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max,
+    void* scratch = nullptr;
+    const sl_status st = stats_scratch(stream, &scratch);
+    if (st != SL_OK) return st;
+    return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max, scratch,
                                           static_cast<hipStream_t>(stream)));
 }
 

@@ -97,14 +97,20 @@ __global__ __launch_bounds__(kWave) void validate_kernel(PeerTable peers, int64_
 
 constexpr int kStatWaves = 4;
 constexpr int kStatThreads = kWave * kStatWaves;
+constexpr int kStatValues = 5;  // four counts and the scale maximum (fp32 bits, widened)
 
-// counts (uint64[n_peers][4]) and the scale maxima (fp32 bit patterns,
-// uint32[n_peers]) start from 0 before the statistics kernel adds to them.
-__global__ __launch_bounds__(kStatThreads) void clear_stats_kernel(uint64_t* counts, uint32_t* scale_max,
-                                                                   int32_t n_peers) {
-    for (int i = (int)threadIdx.x; i < 4 * n_peers; i += kStatThreads) counts[i] = 0ull;
-    for (int i = (int)threadIdx.x; i < n_peers; i += kStatThreads) scale_max[i] = 0u;
-}
+// Scratch layout: the slots (G * n_peers <= kStatGroups + SL_MAX_PEERS - 1,
+// kStatValues uint64 each), then one uint32 arrival counter per peer.  The
+// counters must be zero before the first call; every completed call leaves
+// them at zero.
+// About 256 workgroups in all: at 24 peers x 57344 records 256, 512 and 1024
+// took 31.3, 32.6-33.3 and 32.2-32.9 us.
+constexpr int kStatGroups = 256;
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima): every vector
+// memory access issued so far has completed.
+constexpr int kWaitStoresDone = 0x0F70;
+constexpr size_t kStatSlotBytes = (size_t)(kStatGroups + SL_MAX_PEERS) * kStatValues * sizeof(uint64_t);
+constexpr size_t kStatScratchBytes = kStatSlotBytes + SL_MAX_PEERS * sizeof(uint32_t);
 
 __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 #pragma unroll
@@ -113,14 +119,22 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 }
 
 // Grid (G, n_peers).  Workgroup g of peer p takes records g*256 + t +
-// k*G*256; flags (if given) as validate_kernel writes them.
+// k*G*256; flags (if given) as validate_kernel writes them.  Each workgroup
+// stores its five partial results in its own slot of the scratch, then counts
+// itself in the peer's arrival counter; the workgroup that arrives last (the
+// G-th) adds up the peer's G slots, writes the totals over
+// counts[4p..4p+3] and scale_max[p], and sets the counter back to zero for the
+// next call.  One launch, no clearing pass, and the totals do not depend on
+// the arrival order.
 __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, int64_t n_chunks, uint8_t* flags,
-                                                             uint64_t* counts, uint32_t* scale_max) {
-    __shared__ uint64_t part[kStatWaves][4];
-    __shared__ uint32_t part_max[kStatWaves];
+                                                             uint64_t* counts, uint32_t* scale_max,
+                                                             uint64_t* slots, uint32_t* arrived) {
+    __shared__ uint64_t part[kStatWaves][kStatValues];
+    __shared__ uint32_t last;
     const int p = (int)blockIdx.y;
+    const int G = (int)gridDim.x;
     const int tid = (int)threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kStatThreads;
+    const int64_t stride = (int64_t)G * kStatThreads;
     uint32_t bad = 0, zero = 0, mag = 0, neg = 0, mx = 0;
 #pragma unroll 2
     for (int64_t c = (int64_t)blockIdx.x * kStatThreads + tid; c < n_chunks; c += stride) {
@@ -152,22 +166,64 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, in
         part[wv][1] = t1;
         part[wv][2] = t2;
         part[wv][3] = t3;
-        part_max[wv] = tm;
+        part[wv][4] = tm;
     }
     __syncthreads();
-    // Lanes 0..3 add one count each, lane 4 the maximum: vector atomics,
-    // skipped when there is nothing to add.
-    if (tid < 5) {
-        if (tid < 4) {
-            uint64_t v = 0;
-            for (int i = 0; i < kStatWaves; ++i) v += part[i][tid];
-            if (v) atomicAdd((unsigned long long*)&counts[4 * (size_t)p + tid], (unsigned long long)v);
-        } else {
-            uint32_t m = 0;
-            for (int i = 0; i < kStatWaves; ++i) m = part_max[i] > m ? part_max[i] : m;
-            if (m) atomicMax(&scale_max[p], m);
-        }
+    uint64_t* peer_slots = slots + (size_t)p * (size_t)G * kStatValues;
+    if (tid == 0) {
+        uint64_t* mine = peer_slots + (size_t)blockIdx.x * kStatValues;
+        uint64_t vals[kStatValues];
+        uint64_t m = 0;
+        for (int k = 0; k < 4; ++k) vals[k] = part[0][k] + part[1][k] + part[2][k] + part[3][k];
+        for (int i = 0; i < kStatWaves; ++i) m = part[i][4] > m ? part[i][4] : m;
+        vals[4] = m;
+        // The slots are the only data passed between workgroups, and they go
+        // through agent-scope atomic stores and loads, which the non-coherent
+        // caches do not hold back or serve stale.  So the hand-over needs the
+        // slot stores completed before the count is raised (the wait below),
+        // not the cache write-back and invalidation that release / acquire
+        // orderings add; with those on every workgroup's count the pass took
+        // 35-63 us at 24 peers x 57344 records instead of 31 us.
+        for (int k = 0; k < kStatValues; ++k)
+            __hip_atomic_store(&mine[k], vals[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // no reordering by the compiler
+        __builtin_amdgcn_s_waitcnt(kWaitStoresDone);
+        const uint32_t before = __hip_atomic_fetch_add(&arrived[p], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = before == (uint32_t)(G - 1) ? 1u : 0u;
     }
+    __syncthreads();
+    if (last == 0u) return;  // the whole workgroup
+    // Integer sums and a maximum: any grouping gives the same totals.
+    uint64_t v[kStatValues] = {0, 0, 0, 0, 0};
+    for (int g = tid; g < G; g += kStatThreads) {
+        uint64_t* s = peer_slots + (size_t)g * kStatValues;
+        uint64_t x[kStatValues];
+#pragma unroll
+        for (int k = 0; k < kStatValues; ++k) x[k] = __hip_atomic_load(&s[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] += x[k];
+        v[4] = x[4] > v[4] ? x[4] : v[4];
+    }
+    const uint64_t r0 = wave_sum64(v[0]), r1 = wave_sum64(v[1]), r2 = wave_sum64(v[2]), r3 = wave_sum64(v[3]);
+    const uint32_t r4 = wave_max((uint32_t)v[4]);
+    __syncthreads();  // every wavefront is done reading part[] above
+    if ((tid & (kWave - 1)) == 0) {
+        part[wv][0] = r0;
+        part[wv][1] = r1;
+        part[wv][2] = r2;
+        part[wv][3] = r3;
+        part[wv][4] = r4;
+    }
+    __syncthreads();
+    if (tid < kStatValues) {
+        uint64_t t = 0;
+        for (int i = 0; i < kStatWaves; ++i) t = tid < 4 ? t + part[i][tid] : (part[i][4] > t ? part[i][4] : t);
+        if (tid < 4)
+            counts[4 * (size_t)p + tid] = t;
+        else
+            scale_max[p] = (uint32_t)t;
+    }
+    if (tid == 0) __hip_atomic_store(&arrived[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -181,24 +237,21 @@ hipError_t launch_validate(const PeerTable& peers, int32_t n_peers, int64_t n_ch
                            dim3(kWave), args, 0, stream);
 }
 
+size_t peer_stats_scratch_bytes() { return kStatScratchBytes; }
+
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
-                             int64_t* counts, float* scale_max, hipStream_t stream) {
+                             int64_t* counts, float* scale_max, void* scratch, hipStream_t stream) {
+    const int64_t per_peer = (kStatGroups + n_peers - 1) / n_peers;
+    const int64_t needed = (n_chunks + kStatThreads - 1) / kStatThreads;
+    const int64_t gx = needed < 1 ? 1 : needed < per_peer ? needed : per_peer;
     uint64_t* cnt = reinterpret_cast<uint64_t*>(counts);
     uint32_t* mx = reinterpret_cast<uint32_t*>(scale_max);
-    void* cargs[] = {(void*)&cnt, (void*)&mx, (void*)&n_peers};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&clear_stats_kernel), dim3(1),
-                                   dim3(kStatThreads), cargs, 0, stream);
-    if (e != hipSuccess || n_chunks == 0) return e;
-    // About 1024 workgroups in all, each lane taking several records.  The
-    // totals are device-scope atomics, which are slow across the 8 XCDs: with
-    // 4096 or 8192 workgroups at 24 peers the pass took 50 or 64 us, with 256
-    // to 2048 it took 31-33 us (loop unrolled by 2: 31 us).
-    const int64_t per_peer = (1024 + n_peers - 1) / n_peers;
-    const int64_t needed = (n_chunks + kStatThreads - 1) / kStatThreads;
-    const unsigned gx = (unsigned)(needed < per_peer ? needed : per_peer);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(scratch);
+    uint32_t* arrived = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(scratch) + kStatSlotBytes);
     PeerTable t = peers;
-    void* args[] = {(void*)&t, (void*)&n_chunks, (void*)&flags, (void*)&cnt, (void*)&mx};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&stats_kernel), dim3(gx, (unsigned)n_peers),
+    void* args[] = {(void*)&t, (void*)&n_chunks, (void*)&flags, (void*)&cnt, (void*)&mx, (void*)&slots,
+                    (void*)&arrived};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&stats_kernel), dim3((unsigned)gx, (unsigned)n_peers),
                            dim3(kStatThreads), args, 0, stream);
 }
 

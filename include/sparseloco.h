@@ -236,6 +236,14 @@ sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* cons
  * counts    out int64[n_peers][4] (device, 8-byte aligned), overwritten
  * scale_max out float32[n_peers] (device, 4-byte aligned), overwritten
  * No output may overlap another output or any payload or scale buffer.
+ *
+ * One kernel launch.  Its workgroups hand partial results to each other
+ * through a 15,872-byte device buffer that the library allocates and zeroes on
+ * the first call on each device and keeps until the process ends.  That first
+ * call must not be made while its stream is being captured into a graph
+ * (SL_ERR_HIP); later calls allocate nothing.  All calls on one device share
+ * the buffer, so calls that overlap in time (streams with no ordering between
+ * them) race.
  */
 sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
                         int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
