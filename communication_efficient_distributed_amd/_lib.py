@@ -30,7 +30,7 @@ STATUS = {
 
 EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_apply",
            "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_peer_stats",
-           "sl_host_device_pointer", "sl_status_string")
+           "sl_peer_stats_noalloc", "sl_host_device_pointer", "sl_status_string")
 
 
 class SparseLoCoError(RuntimeError):
@@ -67,6 +67,8 @@ def load():
     L.sl_validate_payloads.restype = ctypes.c_int
     L.sl_peer_stats.argtypes = [P, P, I32, I64, P, P, P, P]
     L.sl_peer_stats.restype = ctypes.c_int
+    L.sl_peer_stats_noalloc.argtypes = [P, P, I32, I64, P, P, P, P]
+    L.sl_peer_stats_noalloc.restype = ctypes.c_int
     L.sl_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
     L.sl_host_device_pointer.restype = ctypes.c_int
     L.sl_aggregate.argtypes = [P, P, I32, P, I64, P]
@@ -202,13 +204,15 @@ def sl_validate_payloads(payloads, scales, flags: torch.Tensor, stream=None) -> 
 
 
 def sl_peer_stats(payloads, scales, counts: torch.Tensor, scale_max: torch.Tensor, flags=None,
-                  n_chunks: int | None = None, stream=None) -> None:
+                  n_chunks: int | None = None, stream=None, noalloc: bool = False) -> None:
     """Per-peer statistics of the received records, one pass.  counts is int64
     [n_peers, 4]: records flagged by validation, records with scale +-0,
     entries at the magnitude level, entries with the sign bit; scale_max is
     float32 [n_peers], the largest finite non-negative scale.  flags, if given,
     is uint8 [n_peers, n_chunks] and receives the validation flags.  n_chunks
-    defaults to the peers' record count (peer 0's, or the PeerSet's)."""
+    defaults to the peers' record count (peer 0's, or the PeerSet's).  With
+    noalloc, sl_peer_stats_noalloc is called instead (the library's static
+    scratch; nothing is allocated)."""
     N = len(payloads)
     if counts.dim() != 2 or tuple(counts.shape) != (N, 4):
         raise ValueError("counts must be a [n_peers, 4] tensor")
@@ -227,9 +231,10 @@ def sl_peer_stats(payloads, scales, counts: torch.Tensor, scale_max: torch.Tenso
     c = _dev(counts, "counts", torch.int64)
     m = _dev(scale_max, "scale_max", torch.float32)
     f = _dev(flags, "flags", torch.uint8) if flags is not None else ctypes.c_void_p(None)
+    name = "sl_peer_stats_noalloc" if noalloc else "sl_peer_stats"
     with torch.cuda.device(counts.device):
-        _check("sl_peer_stats", load().sl_peer_stats(pa, sa, ctypes.c_int32(N), ctypes.c_int64(n_chunks), f, c, m,
-                                                     _stream_of(counts, stream)))
+        _check(name, getattr(load(), name)(pa, sa, ctypes.c_int32(N), ctypes.c_int64(n_chunks), f, c, m,
+                                           _stream_of(counts, stream)))
 
 
 class PeerSet:

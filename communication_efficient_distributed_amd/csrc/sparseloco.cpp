@@ -24,6 +24,45 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 sl_status from_hip(hipError_t e) { return e == hipSuccess ? SL_OK : SL_ERR_HIP; }
 
+// Argument checks of sl_peer_stats and sl_peer_stats_noalloc; fills the
+// pointer table.  *noop is set when there is nothing to do (n_peers == 0).
+sl_status peer_stats_args(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
+                          int64_t n_chunks, const uint8_t* flags, const int64_t* counts, const float* scale_max,
+                          sl::PeerTable* table, bool* noop) {
+    *noop = false;
+    if (n_chunks < 0 || n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n_peers == 0) {
+        *noop = true;
+        return SL_OK;
+    }
+    if (!counts || !scale_max) return SL_ERR_INVALID_ARG;
+    if (!aligned(counts, 8) || !aligned(scale_max, 4)) return SL_ERR_ALIGN;
+    const size_t cbytes = (size_t)n_peers * 4 * sizeof(int64_t);
+    const size_t mbytes = (size_t)n_peers * sizeof(float);
+    const size_t fbytes = flags ? (size_t)n_peers * (size_t)n_chunks : 0;
+    if (overlap(counts, cbytes, scale_max, mbytes) || overlap(flags, fbytes, counts, cbytes) ||
+        overlap(flags, fbytes, scale_max, mbytes))
+        return SL_ERR_INVALID_ARG;
+    if (n_chunks > 0) {
+        if (!payloads || !scales) return SL_ERR_INVALID_ARG;
+        const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
+        const size_t sbytes = (size_t)n_chunks * sizeof(float);
+        for (int32_t p = 0; p < n_peers; ++p) {
+            if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
+            if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
+            const void* bufs[3] = {flags, counts, scale_max};
+            const size_t lens[3] = {fbytes, cbytes, mbytes};
+            for (int b = 0; b < 3; ++b)
+                if (overlap(bufs[b], lens[b], payloads[p], pbytes) || overlap(bufs[b], lens[b], scales[p], sbytes))
+                    return SL_ERR_INVALID_ARG;
+            table->payload[p] = payloads[p];
+            table->scales[p] = scales[p];
+        }
+    }
+    return SL_OK;
+}
+
 // sl_peer_stats's scratch: one buffer per device, allocated and zeroed by the
 // first call on the device and kept until the process ends.  That first call
 // must not be made while its stream is being captured into a graph (it gets
@@ -152,37 +191,26 @@ sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* cons
 
 sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
                         int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max, void* stream) {
-    if (n_chunks < 0 || n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
-    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
-    if (n_peers == 0) return SL_OK;
-    if (!counts || !scale_max) return SL_ERR_INVALID_ARG;
-    if (!aligned(counts, 8) || !aligned(scale_max, 4)) return SL_ERR_ALIGN;
-    const size_t cbytes = (size_t)n_peers * 4 * sizeof(int64_t);
-    const size_t mbytes = (size_t)n_peers * sizeof(float);
-    const size_t fbytes = flags ? (size_t)n_peers * (size_t)n_chunks : 0;
-    if (overlap(counts, cbytes, scale_max, mbytes) || overlap(flags, fbytes, counts, cbytes) ||
-        overlap(flags, fbytes, scale_max, mbytes))
-        return SL_ERR_INVALID_ARG;
     sl::PeerTable table = {};
-    if (n_chunks > 0) {
-        if (!payloads || !scales) return SL_ERR_INVALID_ARG;
-        const size_t pbytes = (size_t)n_chunks * SL_PAYLOAD_BYTES;
-        const size_t sbytes = (size_t)n_chunks * sizeof(float);
-        for (int32_t p = 0; p < n_peers; ++p) {
-            if (!payloads[p] || !scales[p]) return SL_ERR_INVALID_ARG;
-            if (!aligned(payloads[p], 16) || !aligned(scales[p], 4)) return SL_ERR_ALIGN;
-            const void* bufs[3] = {flags, counts, scale_max};
-            const size_t lens[3] = {fbytes, cbytes, mbytes};
-            for (int b = 0; b < 3; ++b)
-                if (overlap(bufs[b], lens[b], payloads[p], pbytes) || overlap(bufs[b], lens[b], scales[p], sbytes))
-                    return SL_ERR_INVALID_ARG;
-            table.payload[p] = payloads[p];
-            table.scales[p] = scales[p];
-        }
-    }
+    bool noop = false;
+    const sl_status st = peer_stats_args(payloads, scales, n_peers, n_chunks, flags, counts, scale_max, &table, &noop);
+    if (st != SL_OK || noop) return st;
     void* scratch = nullptr;
-    const sl_status st = stats_scratch(stream, &scratch);
-    if (st != SL_OK) return st;
+    const sl_status ss = stats_scratch(stream, &scratch);
+    if (ss != SL_OK) return ss;
+    return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max, scratch,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+sl_status sl_peer_stats_noalloc(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
+                                int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
+                                void* stream) {
+    sl::PeerTable table = {};
+    bool noop = false;
+    const sl_status st = peer_stats_args(payloads, scales, n_peers, n_chunks, flags, counts, scale_max, &table, &noop);
+    if (st != SL_OK || noop) return st;
+    void* scratch = nullptr;  // the library's static copy on the current device
+    if (sl::peer_stats_static_scratch(&scratch) != hipSuccess) return SL_ERR_HIP;
     return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max, scratch,
                                           static_cast<hipStream_t>(stream)));
 }

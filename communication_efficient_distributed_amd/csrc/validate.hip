@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "sparseloco.h"
 #include "wave.h"
@@ -111,6 +113,12 @@ constexpr int kStatGroups = 256;
 constexpr int kWaitStoresDone = 0x0F70;
 constexpr size_t kStatSlotBytes = (size_t)(kStatGroups + SL_MAX_PEERS) * kStatValues * sizeof(uint64_t);
 constexpr size_t kStatScratchBytes = kStatSlotBytes + SL_MAX_PEERS * sizeof(uint32_t);
+
+// sl_peer_stats_noalloc's scratch: one copy on every GPU the library runs on,
+// zero when the code object is loaded (its counters must start at zero, and
+// every completed call leaves them at zero).  Host code uses the address
+// hipGetSymbolAddress returns for the current device, never this name.
+static __device__ __align__(256) uint8_t scratch[kStatScratchBytes];
 
 __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 #pragma unroll
@@ -239,15 +247,38 @@ hipError_t launch_validate(const PeerTable& peers, int32_t n_peers, int64_t n_ch
 
 size_t peer_stats_scratch_bytes() { return kStatScratchBytes; }
 
+hipError_t peer_stats_static_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
-                             int64_t* counts, float* scale_max, void* scratch, hipStream_t stream) {
+                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream) {
     const int64_t per_peer = (kStatGroups + n_peers - 1) / n_peers;
     const int64_t needed = (n_chunks + kStatThreads - 1) / kStatThreads;
     const int64_t gx = needed < 1 ? 1 : needed < per_peer ? needed : per_peer;
+    static_assert((size_t)(kStatGroups + SL_MAX_PEERS - 1) * kStatValues * sizeof(uint64_t) <= kStatSlotBytes,
+                  "the slots of every valid call fit the scratch");
+    if (gx * n_peers > kStatGroups + SL_MAX_PEERS - 1) return hipErrorInvalidValue;
     uint64_t* cnt = reinterpret_cast<uint64_t*>(counts);
     uint32_t* mx = reinterpret_cast<uint32_t*>(scale_max);
-    uint64_t* slots = reinterpret_cast<uint64_t*>(scratch);
-    uint32_t* arrived = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(scratch) + kStatSlotBytes);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(scratch_ptr);
+    uint32_t* arrived = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(scratch_ptr) + kStatSlotBytes);
     PeerTable t = peers;
     void* args[] = {(void*)&t, (void*)&n_chunks, (void*)&flags, (void*)&cnt, (void*)&mx, (void*)&slots,
                     (void*)&arrived};

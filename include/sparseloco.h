@@ -250,6 +250,27 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
                         void* stream);
 
 /*
+ * sl_peer_stats_noalloc -- sl_peer_stats for callers that cannot allocate
+ * device memory: code under graph capture (including a first call), tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, checks,
+ * results and single kernel launch as sl_peer_stats; it calls no hipMalloc,
+ * hipFree or other allocating routine.
+ *
+ * Its scratch is a static device array of 15,872 bytes on every GPU the library
+ * runs on, held until the process ends.  Every valid call fits in it
+ * (n_peers <= SL_MAX_PEERS, any n_chunks), so no size is refused beyond the
+ * checks above.  All calls on one GPU share that GPU's array: calls that
+ * overlap in time there (streams with no ordering between them, or with a
+ * concurrent sl_peer_stats_noalloc from another thread) race.  Its arrival
+ * counters are zero when the library is loaded and every completed call leaves
+ * them at zero.  It does not share scratch with sl_peer_stats.
+ * Returns SL_ERR_HIP if the array's device address cannot be found.
+ */
+sl_status sl_peer_stats_noalloc(const uint8_t* const* payloads, const float* const* scales,
+                                int32_t n_peers, int64_t n_chunks, uint8_t* flags, int64_t* counts,
+                                float* scale_max, void* stream);
+
+/*
  * sl_host_device_pointer -- device address of pinned, mapped host memory.
  *
  * Error-feedback offload ([CV] "SparseLoCo: Breaking the Bandwidth Barrier":

@@ -243,9 +243,11 @@ def test_validate_many_argument_checks(lib):
     assert lib.sl_validate_payloads(None, None, 2, 16, F, None) == SL_ERR_INVALID_ARG
 
 
-def test_peer_stats_argument_checks(lib):
+@pytest.mark.parametrize("name", ["sl_peer_stats", "sl_peer_stats_noalloc"])
+def test_peer_stats_argument_checks(lib, name):
     """Every call here is rejected (or is a no-op) on the host, before any
-    launch."""
+    launch (and, for sl_peer_stats, before its scratch is allocated)."""
+    fn = getattr(lib, name)
     F = A * 1200
     CNT = A * 1300
     MX = A * 1400
@@ -255,8 +257,8 @@ def test_peer_stats_argument_checks(lib):
     def call(peers, scales, n_peers, n_chunks=16, flags=F, counts=CNT, smax=MX):
         pa = (ctypes.c_void_p * max(len(peers), 1))(*peers)
         sa = (ctypes.c_void_p * max(len(scales), 1))(*scales)
-        return lib.sl_peer_stats(ctypes.cast(pa, ctypes.c_void_p), ctypes.cast(sa, ctypes.c_void_p),
-                                 n_peers, n_chunks, flags, counts, smax, None)
+        return fn(ctypes.cast(pa, ctypes.c_void_p), ctypes.cast(sa, ctypes.c_void_p),
+                  n_peers, n_chunks, flags, counts, smax, None)
 
     assert call(pp, ss, 3, n_chunks=-1) == SL_ERR_SHAPE
     assert call(pp, ss, 3, n_chunks=1 << 31) == SL_ERR_SHAPE
@@ -276,7 +278,7 @@ def test_peer_stats_argument_checks(lib):
     assert call(pp, ss, 3, counts=pp[1] + 16) == SL_ERR_INVALID_ARG     # counts inside a record buffer
     assert call(pp, ss, 3, smax=ss[2]) == SL_ERR_INVALID_ARG            # scale_max on a scale buffer
     assert call(pp, ss, 3, flags=pp[0]) == SL_ERR_INVALID_ARG           # flags on a record buffer
-    assert lib.sl_peer_stats(None, None, 2, 16, None, CNT, MX, None) == SL_ERR_INVALID_ARG
+    assert fn(None, None, 2, 16, None, CNT, MX, None) == SL_ERR_INVALID_ARG
 
 
 def test_peerset_checks_once_and_rejects_bad_tensors():
