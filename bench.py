@@ -517,6 +517,30 @@ def workloads(sl, dev, shapes, done=lambda what: None, reps=10):
         t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate(peers, None, out), k=reps)
         r["aggregate"] = st(n, t, BYTES_AGGREGATE, ts)
         if W == datagen.DECODER_BLOCK:
+            # One 581 MB record set read call after call stays partly in the
+            # 256 MB last-level cache; a second set, alternated with the first,
+            # makes every call read its records from HBM.
+            pp2, ps2 = [], []
+            for p in range(N_PEERS + 1, 2 * N_PEERS + 1):
+                datagen.fill_lognormal_(a, W, p, 0)
+                ef.zero_()
+                pl, sc = sl.compress(a, ef, BETA)
+                pp2.append(pl)
+                ps2.append(sc)
+            sets = [peers, sl.PeerSet(pp2, ps2)]
+            turn = [0]
+
+            def cold_call():
+                turn[0] += 1
+                sl.sl_aggregate(sets[turn[0] % 2], None, out)
+
+            t, ts = timed_calls(torch, stream, cold_call, k=reps)
+            r["aggregate_cold"] = dict(st(n, t, BYTES_AGGREGATE, ts), record_sets=2,
+                                       note="two 24-peer record sets alternated, each call's records from HBM; "
+                                            "'aggregate' re-reads one set, which stays partly cache-resident")
+            del sets, pp2, ps2
+            datagen.fill_lognormal_(a, W, 0, 0)
+            ef.zero_()
             theta = ef
             theta.copy_(a).mul_(0.02)
             t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate_apply(peers, None, theta), k=reps)
@@ -827,10 +851,10 @@ def _counter_dispatches(path):
 def _chunks_of(kernel, grid_items, wg):
     """Chunks covered by one launch of an sl:: kernel (grids are padded to a
     multiple of 8 workgroups, one per XCD; the run kernel sums 2 or 3 chunks per
-    wavefront)."""
+    wavefront; beyond 81 peers one)."""
     groups = grid_items // max(wg, 1)
     if "aggregate_run_kernel" in kernel:
-        cpw = 2 if "<9, 2>" in kernel else 3
+        cpw = 2 if "<9, 2>" in kernel else 1 if "<15, 1>" in kernel else 3
         cands = [c for c in WORKLOAD_CHUNKS if ((c + cpw - 1) // cpw + 7) // 8 * 8 == groups]
     else:
         cands = [c for c in WORKLOAD_CHUNKS if (c + 7) // 8 * 8 == groups or c == groups]
@@ -882,6 +906,16 @@ def _label_mlp(dispatches, line):
         if label:
             out.append((label, d))
     return out
+
+
+def _label_decoder(ds):
+    """The decoder block's 24-peer aggregate dispatches in call order: the first
+    half re-read one record set, the second half alternate two (records from
+    HBM)."""
+    dec = [d for d in ds if _sl_key(d["kernel"]).startswith("aggregate_run_kernel") and
+           _chunks_of(d["kernel"], d["grid"], d["wg"]) == DECODER_PARAMS // CHUNK]
+    half = len(dec) // 2
+    return [("decoder_one_set", d) for d in dec[:half]] + [("decoder_two_sets", d) for d in dec[half:]]
 
 
 def _calibration(dispatches, counter):
@@ -1015,21 +1049,17 @@ def summarize_counters(base, outdir):
         written.append(path)
     # Run kernels: the decoder block (24 peers) and the many-peer aggregate.
     run_sections = []
-    for d in lines_of["fetch"]:
-        name = _sl_key(d["kernel"])
-        if not name.startswith("aggregate_run_kernel") and not (name.startswith("aggregate_kernel<")
-                                                                  and name.endswith("false>")):
-            continue
-        chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
-        if chunks == 208896 and name.startswith("aggregate_run_kernel"):
-            run_sections.append(("decoder block, 24 peers", name, d, DECODER_PARAMS, 24))
+    dec_label = {"decoder_one_set": "decoder block, 24 peers, one record set re-read (partly cached)",
+                 "decoder_two_sets": "decoder block, 24 peers, two record sets alternated (records from HBM)"}
+    for lab, d in _label_decoder(lines_of["fetch"]):
+        run_sections.append((dec_label[lab], _sl_key(d["kernel"]), d, DECODER_PARAMS, 24))
     many = line.get("workloads", {}).get("mlp_many_peers", {})
     counts = [int(k) for k in many if k.isdigit()]
     if counts:
         # the many-peer section calls sl_aggregate 3 + reps times per count, in MANY_PEERS order
         ds = [d for d in lines_of["fetch"] if _chunks_of(d["kernel"], d["grid"], d["wg"]) == C and
               _sl_key(d["kernel"]).startswith(("aggregate_run_kernel", "aggregate_kernel<")) and
-              _sl_key(d["kernel"]).endswith(("false>", "3>", "2>"))]
+              _sl_key(d["kernel"]).endswith(("false>", "3>", "2>", "1>"))]
         taken = sum(1 for lab, _ in labelled if lab in ("aggregate", "aggregate_cold"))
         ds = ds[taken:]
         per = len(ds) // len(counts) if counts else 0
@@ -1063,9 +1093,10 @@ def summarize_trace(base, outdir):
     ds = [{"kernel": r["Kernel_Name"], "grid": int(r["Grid_Size_X"]), "wg": int(r["Workgroup_Size_X"]),
            "peers": int(r["Grid_Size_Y"]), "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3}
           for r in rows if "sl::" in r["Kernel_Name"]]
-    role = {id(d): lab for lab, d in _label_mlp(ds, line)}
+    role = {id(d): lab for lab, d in _label_mlp(ds, line) + _label_decoder(ds)}
     suffix = {"aggregate": ", records cached", "aggregate_cold": ", records from HBM",
-              "compress_host_ef": ", ef in host memory"}
+              "compress_host_ef": ", ef in host memory", "decoder_one_set": ", one record set re-read",
+              "decoder_two_sets": ", two record sets alternated"}
     timed_of = {"compress_timed": "compress_kernel<false> [8192x28672, timed steps only]",
                 "aggregate_timed": "step aggregate [8192x28672, records cached, timed steps only]"}
     groups = {}

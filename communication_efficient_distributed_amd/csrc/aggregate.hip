@@ -361,8 +361,10 @@ __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, i
 // Three chunks per wavefront hold 98 registers per lane at 24 peers and 151 at
 // 54.  From 55 to 81 peers two chunks per wavefront (147 registers) measured
 // 300-363 us against 330-373 us for one (55-81 peers at 8192 x 28672).
-// Beyond 81 peers two chunks' records need 256 registers and took 637-830 us
-// against 464-562 us, so the one-chunk kernel is used.
+// Beyond 81 peers one chunk per wavefront: the run kernel's form (each lane's
+// peer pointers selected once, then the loads) took 496-498 us at 128 peers
+// against 509-532 us for aggregate_kernel, whose pointers are selected group
+// by group; two chunks per wavefront took 533 us.
 constexpr uint64_t kCachedRecordBytes = 224ull << 20;
 constexpr int kChunksPerWave = 3;
 constexpr int kRunMaxPeers = kPeersPerLoad * 6;       // three chunks per wavefront up to here
@@ -494,9 +496,8 @@ hipError_t launch_aggregate_one(const PeerTable& peers, int32_t n_peers, float* 
         }
     }
     if constexpr (!APPLY) {
-        if (n_peers <= kPairMaxPeers &&
-            (uint64_t)n_peers * (uint64_t)n_chunks * (SL_PAYLOAD_BYTES + sizeof(float)) > kCachedRecordBytes) {
-            const int R = n_peers <= kRunMaxPeers ? kChunksPerWave : 2;
+        if ((uint64_t)n_peers * (uint64_t)n_chunks * (SL_PAYLOAD_BYTES + sizeof(float)) > kCachedRecordBytes) {
+            const int R = n_peers <= kRunMaxPeers ? kChunksPerWave : n_peers <= kPairMaxPeers ? 2 : 1;
             const int64_t runs = (n_chunks + R - 1) / R;
             int64_t run_per_xcd = (runs + kXcds - 1) / kXcds;
             void* pargs[] = {(void*)&t, (void*)&n_peers, (void*)&dst, (void*)&n_chunks, (void*)&run_per_xcd};
@@ -505,7 +506,8 @@ hipError_t launch_aggregate_one(const PeerTable& peers, int32_t n_peers, float* 
                              : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_run_kernel<2, R3>)
                              : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_run_kernel<3, R3>)
                              : n_peers <= kRunMaxPeers      ? reinterpret_cast<const void*>(&aggregate_run_kernel<6, R3>)
-                                                            : reinterpret_cast<const void*>(&aggregate_run_kernel<9, 2>);
+                             : n_peers <= kPairMaxPeers     ? reinterpret_cast<const void*>(&aggregate_run_kernel<9, 2>)
+                                                            : reinterpret_cast<const void*>(&aggregate_run_kernel<15, 1>);
             return hipLaunchKernel(kp, dim3((unsigned)(run_per_xcd * kXcds)), dim3(kWave), pargs, 0, stream);
         }
     }

@@ -39,7 +39,7 @@ COMPRESS = "void sl::(anonymous namespace)::compress_kernel<false>(float const*,
 AGG = "void sl::(anonymous namespace)::aggregate_kernel<3, false>(sl::PeerTable, int, float*, long, long, float)"
 MEAN = "sl::(anonymous namespace)::apply_mean_kernel(float*, float const*, float, long)"
 RUN63 = "void sl::(anonymous namespace)::aggregate_run_kernel<6, 3>(sl::PeerTable, int, float*, long, long)"
-AGG15 = "void sl::(anonymous namespace)::aggregate_kernel<15, false>(sl::PeerTable, int, float*, long, long, float)"
+RUN151 = "void sl::(anonymous namespace)::aggregate_run_kernel<15, 1>(sl::PeerTable, int, float*, long, long)"
 RUN_ITEMS = ((C + 2) // 3 + 7) // 8 * 8 * 64
 COPY = "__amd_rocclr_copyBuffer"
 TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >(int, at::native::FillFunctor<float>, std::array<char*, 2ul>)"
@@ -58,7 +58,7 @@ SEQUENCE = (
     + [(MEAN, C * 256, 256, 8 * N / 2048, 4 * N / 1024, 430.0)] * (W + K)
     # the many-peer section: 36 peers (three chunks per wavefront), then 128 (one), 3 + 2 calls each
     + [(RUN63, RUN_ITEMS, 64, 36 * REC * N / 2048, 4 * N / 1024, 240.0)] * 5
-    + [(AGG15, AGG_ITEMS, 64, 128 * REC * N / 2048, 4 * N / 1024, 560.0)] * 5
+    + [(RUN151, AGG_ITEMS, 64, 128 * REC * N / 2048, 4 * N / 1024, 500.0)] * 5
 )
 
 
@@ -141,7 +141,7 @@ def test_many_peer_sections_take_the_timed_calls_of_each_count(summary):
     out, _ = summary
     txt = (out / "aggregate_beyond_cache_counters.txt").read_text()
     for label in ("[8192 x 28672, 36 peers: aggregate_run_kernel<6, 3>]",
-                  "[8192 x 28672, 128 peers: aggregate_kernel<15, false>]"):
+                  "[8192 x 28672, 128 peers: aggregate_run_kernel<15, 1>]"):
         block = txt.split(label)[1].split("\n[")[0]
         assert "dispatches_sampled: 2" in block and "ratio 1.000" in block
 
