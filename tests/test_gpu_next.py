@@ -180,6 +180,37 @@ def test_peer_stats_shapes(orc, N, C):
     check_peer_stats(sl, orc, payloads, scales, with_flags=(N * C <= 200000))
 
 
+def test_peer_stats_calls_in_a_row(orc):
+    """Twenty calls on one stream alternating two shapes (24 peers x 3000
+    records, 128 x 40): every call leaves the scratch's arrival counters at
+    zero for the next, and every result matches the oracle."""
+    sl = require_gpu()
+    shapes = []
+    for N, C, seed in ((24, 3000, 61), (128, 40, 62)):
+        payloads, scales = [], []
+        for p in range(N):
+            idx, code, sc = datagen.random_entries_bulk(C, seed * 1000 + p)
+            sc = sc.copy()
+            sc[p % C] = 0.0
+            payloads.append(orc.pack(idx, code))
+            scales.append(sc.astype(np.float32))
+        want = [orc.peer_stats(pl, sc) for pl, sc in zip(payloads, scales)]
+        peers = sl.PeerSet([torch.from_numpy(x).cuda() for x in payloads],
+                           [torch.from_numpy(x).cuda() for x in scales])
+        shapes.append((N, peers, want))
+    for k in range(20):
+        N, peers, want = shapes[k % 2]
+        counts = torch.full((N, 4), -1, dtype=torch.int64, device="cuda")
+        smax = torch.full((N,), -1.0, dtype=torch.float32, device="cuda")
+        note(f"sl_peer_stats call {k}: {N} peers")
+        sl.sl_peer_stats(peers, None, counts, smax)
+        torch.cuda.synchronize()
+        got_c, got_m = counts.cpu().numpy(), smax.cpu().numpy()
+        for p in range(N):
+            assert got_c[p].tolist() == want[p][0].tolist(), f"call {k}: counts of peer {p}"
+            assert_bitwise(got_m[p:p + 1], np.float32([want[p][1]]), f"call {k}: scale_max of peer {p}")
+
+
 def test_peer_stats_without_records():
     """n_chunks = 0: the statistics are still written, all zero."""
     sl = require_gpu()
