@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0            # MI355X published HBM3E bandwidth
 N_PEERS = 24
 BETA = 0.95
 CHUNK = 4096
-RECORD = 112 + 4                 # payload bytes + fp32 scale per chunk
+PAYLOAD = 112                    # record bytes per chunk (12-bit indices, 2-bit codes)
+RECORD = PAYLOAD + 4             # payload bytes + fp32 scale per chunk
 
 # Algorithmic bytes per parameter (what the method must move).
 BYTES_COMPRESS = 4 + 4 + 4 + RECORD / CHUNK           # read delta, ef; write ef; record
@@ -174,6 +175,7 @@ def main():
     # aggregate: 4 sets x 160 MB exceed the last-level cache, so each call's
     # records come from HBM.
     cold_sets = [sl.PeerSet(peer_p, peer_s)]
+    cold_lists = [(peer_p, peer_s)]
     for k in range(1, max(1, args.cold_sets)):
         cp, cs = [], []
         for p in range(k * N_PEERS + 1, (k + 1) * N_PEERS + 1):
@@ -184,6 +186,7 @@ def main():
             cs.append(s)
             del d
         cold_sets.append(sl.PeerSet(cp, cs))
+        cold_lists.append((cp, cs))
     del scratch_ef
     torch.cuda.synchronize()
     stage(args, f"setup: {len(cold_sets)} record sets of {N_PEERS} peers")
@@ -241,7 +244,30 @@ def main():
     t_cc = [e[0].elapsed_time(e[1]) for e in cevs]
     t_ac = [e[1].elapsed_time(e[2]) for e in cevs]
     ms_per_step_cold = cevs[0][0].elapsed_time(cevs[-1][2]) / K
-    stage(args, f"{K} timed steps, cached and cold records")
+
+    # Once more with the same record sets laid out chunk-major across peers
+    # (sl_aggregate_interleaved), copied into that layout here.
+    il_sets = [interleaved_records(torch, p_, s_) for p_, s_ in cold_lists]
+
+    def step_cold_il(k, ev):
+        ev[0].record(stream)
+        sl.sl_compress(delta, ef, BETA, payload, scales)
+        ev[1].record(stream)
+        r_, s_ = il_sets[k % len(il_sets)]
+        sl.sl_aggregate_interleaved(r_, s_, out)
+        ev[2].record(stream)
+
+    for k in range(len(il_sets)):
+        step_cold_il(k, [torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    ievs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for k in range(K):
+        step_cold_il(k, ievs[k])
+    torch.cuda.synchronize()
+    t_ai = [e[1].elapsed_time(e[2]) for e in ievs]
+    t_ci = [e[0].elapsed_time(e[1]) for e in ievs]
+    ms_per_step_cold_il = ievs[0][0].elapsed_time(ievs[-1][2]) / K
+    del il_sets
+    stage(args, f"{K} timed steps, cached and cold records (per peer and chunk-major)")
 
     # The outer update, outside the step: same K, one event pair per call.
     for _ in range(args.warmup):
@@ -277,6 +303,12 @@ def main():
                              "256 MB last-level cache: the records come from HBM"})
     step_cold_stats = kstats(ms_per_step_cold, BYTES_COMPRESS + BYTES_AGGREGATE)
     step_cold_stats["compress_ms"] = round(avg(t_cc), 5)
+    agg_cold_il = kstats(avg(t_ai), BYTES_AGGREGATE, t_ai)
+    agg_cold_il.update({"record_sets": len(cold_sets),
+                        "note": "the same record sets laid out chunk-major across peers "
+                                "(sl_aggregate_interleaved): one contiguous span of records per chunk"})
+    step_cold_il_stats = kstats(ms_per_step_cold_il, BYTES_COMPRESS + BYTES_AGGREGATE)
+    step_cold_il_stats["compress_ms"] = round(avg(t_ci), 5)
     traffic = traffic_from_profile(n)
     result = {
         "metric": METRIC,
@@ -316,6 +348,8 @@ def main():
             "compress_plus_aggregate": kstats(tc + ta, BYTES_COMPRESS + BYTES_AGGREGATE),
             "aggregate_cold": agg_cold,
             "step_cold": step_cold_stats,
+            "aggregate_cold_interleaved": agg_cold_il,
+            "step_cold_interleaved": step_cold_il_stats,
         },
         "warmup_trace": {
             "steps": args.warmup,
@@ -445,6 +479,18 @@ def host_link_dma(torch, host_a, dev, stream, reps=3):
     return r
 
 
+def interleaved_records(torch, payloads, scales):
+    """The peers' per-peer records and scales copied into the chunk-major layout
+    of sl_aggregate_interleaved: uint8 [C, P, 112] and float32 [C, P]."""
+    C, P = scales[0].numel(), len(payloads)
+    rec = torch.empty((C, P, PAYLOAD), dtype=torch.uint8, device=scales[0].device)
+    sc = torch.empty((C, P), dtype=torch.float32, device=scales[0].device)
+    for k in range(P):
+        rec[:, k, :].copy_(payloads[k].view(C, PAYLOAD))
+        sc[:, k].copy_(scales[k])
+    return rec, sc
+
+
 def timed_calls(torch, stream, fn, k=20, warm=3):
     """Mean and per-call times (ms) of fn, each call timed on its own behind a
     short spin kernel, so that host-side argument marshalling (pointer tables
@@ -538,7 +584,17 @@ def workloads(sl, dev, shapes, done=lambda what: None, reps=10):
             r["aggregate_cold"] = dict(st(n, t, BYTES_AGGREGATE, ts), record_sets=2,
                                        note="two 24-peer record sets alternated, each call's records from HBM; "
                                             "'aggregate' re-reads one set, which stays partly cache-resident")
-            del sets, pp2, ps2
+            il = [interleaved_records(torch, pp, ps), interleaved_records(torch, pp2, ps2)]
+
+            def cold_il_call():
+                turn[0] += 1
+                r_, s_ = il[turn[0] % 2]
+                sl.sl_aggregate_interleaved(r_, s_, out)
+
+            t, ts = timed_calls(torch, stream, cold_il_call, k=reps)
+            r["aggregate_cold_interleaved"] = dict(st(n, t, BYTES_AGGREGATE, ts), record_sets=2,
+                                                   note="the same two sets laid out chunk-major across peers")
+            del sets, pp2, ps2, il
             datagen.fill_lognormal_(a, W, 0, 0)
             ef.zero_()
             theta = ef
@@ -600,6 +656,24 @@ def many_peers(sl, dev, reps):
         gbs = bpp * n / (t * 1e-3) / 1e9
         res[str(P)] = {"ms": round(t, 5), "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                        "bytes_per_param": round(bpp, 4), "record_mb": round(P * C * RECORD / 1e6, 1)}
+    # The same records laid out chunk-major across peers (sl_aggregate_interleaved).
+    il = {}
+    for P in MANY_PEERS:
+        r_, s_ = interleaved_records(torch, pp[:P], ps[:P])
+        for _ in range(3):
+            sl.sl_aggregate_interleaved(r_, s_, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sl.sl_aggregate_interleaved(r_, s_, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps
+        bpp = 4 + P * RECORD / CHUNK
+        gbs = bpp * n / (t * 1e-3) / 1e9
+        il[str(P)] = {"ms": round(t, 5), "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del r_, s_
+    res["interleaved"] = il
     del pp, ps, out
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -853,8 +927,8 @@ def _chunks_of(kernel, grid_items, wg):
     multiple of 8 workgroups, one per XCD; the run kernel sums 2 or 3 chunks per
     wavefront; beyond 81 peers one)."""
     groups = grid_items // max(wg, 1)
-    if "aggregate_run_kernel" in kernel:
-        cpw = 2 if "<9, 2>" in kernel else 1 if "<15, 1>" in kernel else 3
+    if "aggregate_run_kernel" in kernel or "aggregate_interleaved_kernel" in kernel:
+        cpw = int(kernel.split("<")[1].split(">")[0].split(",")[1])   # <NGMAX, chunks per wavefront>
         cands = [c for c in WORKLOAD_CHUNKS if ((c + cpw - 1) // cpw + 7) // 8 * 8 == groups]
     else:
         cands = [c for c in WORKLOAD_CHUNKS if (c + 7) // 8 * 8 == groups or c == groups]
@@ -872,7 +946,8 @@ def _label_mlp(dispatches, line):
     in bench.py's run, from its fixed call order."""
     W, K, S = line["warmup"], line["steps"], line["kernels"]["aggregate_cold"]["record_sets"]
     peers = line["config"]["peers"]
-    n_step = peers * S + W + K + S + K       # setup, warmup, timed, cold-step compressions
+    n_il = S + K if "aggregate_cold_interleaved" in line["kernels"] else 0
+    n_step = peers * S + W + K + S + K + n_il    # setup, warmup, timed, cold and chunk-major cold steps
     n_host = 6 if "next_rows" in line else 0  # then the host-resident EF row: 1 warmup + 5 timed
     C = MLP_PARAMS // CHUNK
     seen = {}
@@ -885,7 +960,8 @@ def _label_mlp(dispatches, line):
         chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
         if step_agg is None and chunks == C and name.startswith("aggregate_kernel<") and name.endswith("false>"):
             step_agg = name
-        key = (name, chunks)
+        # every chunk-major aggregate variant shares one count (the step's calls come first)
+        key = ("aggregate_interleaved_kernel" if name.startswith("aggregate_interleaved_kernel") else name, chunks)
         i = seen.get(key, 0)
         seen[key] = i + 1
         label = None
@@ -903,6 +979,8 @@ def _label_mlp(dispatches, line):
                 label = "aggregate_apply"
             elif name == "compress_kernel<true>":
                 label = "compress_weights"
+            elif name.startswith("aggregate_interleaved_kernel") and i < n_il:
+                label = "aggregate_cold_interleaved"
         if label:
             out.append((label, d))
     return out
@@ -1016,6 +1094,8 @@ def summarize_counters(base, outdir):
         "compress_weights": ("compress_kernel<true>", 12.0, 4.0 + RECORD / CHUNK, "compress"),
         "aggregate": ("aggregate_kernel, records cache-resident (the same 24 peers every call)", rec, 4.0, "aggregate"),
         "aggregate_cold": ("aggregate_kernel, records from HBM (four rotating record sets)", rec, 4.0, "aggregate"),
+        "aggregate_cold_interleaved": ("aggregate_interleaved_kernel, records from HBM laid out chunk-major across "
+                                       "peers (the same four sets)", rec, 4.0, "aggregate"),
         "apply_mean": ("apply_mean_kernel", 8.0, 4.0, "aggregate"),
         "aggregate_apply": ("aggregate_apply4_kernel", 4.0 + rec, 4.0, "aggregate"),
     }
@@ -1040,8 +1120,11 @@ def summarize_counters(base, outdir):
     for role, fname in files.items():
         if role not in sections:
             continue
-        body = sections[role] + ([""] + sections["aggregate_cold"] if role == "aggregate" and
-                                 "aggregate_cold" in sections else [])
+        body = list(sections[role])
+        if role == "aggregate":
+            for extra in ("aggregate_cold", "aggregate_cold_interleaved"):
+                if extra in sections:
+                    body += [""] + sections[extra]
         lines = _header(f"{roles[role][0].split(',')[0]}, 8192 x 28672 fp32 ({n:,} params), {P} peers", cal) + [""] + body
         path = os.path.join(outdir, fname)
         with open(path, "w") as f:
@@ -1066,6 +1149,22 @@ def summarize_counters(base, outdir):
         for j, Pm in enumerate(sorted(counts)):
             for d in ds[j * per:(j + 1) * per][3:]:
                 run_sections.append((f"8192 x 28672, {Pm} peers", _sl_key(d["kernel"]), d, n, Pm))
+    # Chunk-major records (sl_aggregate_interleaved): after the step's cold
+    # calls, the decoder block's two alternated sets and the many-peer counts.
+    il_ds = [d for d in lines_of["fetch"] if _sl_key(d["kernel"]).startswith("aggregate_interleaved_kernel")]
+    for d in il_ds:
+        if _chunks_of(d["kernel"], d["grid"], d["wg"]) == DECODER_PARAMS // CHUNK:
+            run_sections.append(("decoder block, 24 peers, two record sets alternated, chunk-major",
+                                 _sl_key(d["kernel"]), d, DECODER_PARAMS, 24))
+    il_counts = sorted(int(k) for k in many.get("interleaved", {}))
+    if il_counts:
+        n_il = line["kernels"]["aggregate_cold_interleaved"]["record_sets"] + line["steps"] \
+            if "aggregate_cold_interleaved" in line["kernels"] else 0
+        mlp_il = [d for d in il_ds if _chunks_of(d["kernel"], d["grid"], d["wg"]) == C][n_il:]
+        per = len(mlp_il) // len(il_counts)
+        for j, Pm in enumerate(il_counts):
+            for d in mlp_il[j * per:(j + 1) * per][3:]:
+                run_sections.append((f"8192 x 28672, {Pm} peers, chunk-major", _sl_key(d["kernel"]), d, n, Pm))
     if run_sections:
         lines = _header("aggregate kernels with records beyond the last-level cache", cal)
         lines += [f"aggregate_code_sha256_16: {code_digest(_kernel_sources('aggregate'))}   "
@@ -1096,6 +1195,7 @@ def summarize_trace(base, outdir):
     role = {id(d): lab for lab, d in _label_mlp(ds, line) + _label_decoder(ds)}
     suffix = {"aggregate": ", records cached", "aggregate_cold": ", records from HBM",
               "compress_host_ef": ", ef in host memory", "decoder_one_set": ", one record set re-read",
+              "aggregate_cold_interleaved": ", records from HBM, chunk-major",
               "decoder_two_sets": ", two record sets alternated"}
     timed_of = {"compress_timed": "compress_kernel<false> [8192x28672, timed steps only]",
                 "aggregate_timed": "step aggregate [8192x28672, records cached, timed steps only]"}

@@ -28,7 +28,7 @@ STATUS = {
     5: "SL_ERR_HIP",
 }
 
-EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_apply",
+EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_interleaved", "sl_aggregate_apply",
            "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_peer_stats",
            "sl_peer_stats_noalloc", "sl_host_device_pointer", "sl_status_string")
 
@@ -73,6 +73,8 @@ def load():
     L.sl_host_device_pointer.restype = ctypes.c_int
     L.sl_aggregate.argtypes = [P, P, I32, P, I64, P]
     L.sl_aggregate.restype = ctypes.c_int
+    L.sl_aggregate_interleaved.argtypes = [P, P, I32, P, I64, P]
+    L.sl_aggregate_interleaved.restype = ctypes.c_int
     L.sl_aggregate_apply.argtypes = [P, P, I32, P, I64, P]
     L.sl_aggregate_apply.restype = ctypes.c_int
     L.sl_apply_mean.argtypes = [P, P, I32, I64, P]
@@ -297,6 +299,28 @@ def sl_aggregate(payloads, scales, out: torch.Tensor, stream=None) -> None:
     with torch.cuda.device(out.device):
         _check("sl_aggregate", load().sl_aggregate(pa, sa, ctypes.c_int32(N), o, ctypes.c_int64(n),
                                                    _stream_of(out, stream)))
+
+
+def sl_aggregate_interleaved(records: torch.Tensor, scales: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """sl_aggregate on records laid out chunk-major across peers: records is
+    uint8 [n/4096, n_peers, 112] and scales float32 [n/4096, n_peers]; out is
+    float32 [n].  The same sums as sl_aggregate on the per-peer buffers."""
+    if records.dim() != 3 or records.shape[2] != SL_PAYLOAD_BYTES:
+        raise ValueError("records must be a [n_chunks, n_peers, 112] tensor")
+    C, N = records.shape[0], records.shape[1]
+    if scales.dim() != 2 or tuple(scales.shape) != (C, N):
+        raise ValueError("scales must be a [n_chunks, n_peers] tensor")
+    n = out.numel()
+    if n != C * SL_CHUNK:
+        raise ValueError("out must hold n_chunks * 4096 floats")
+    o = _dev(out, "out", torch.float32)
+    if N:
+        r, s = _dev(records, "records", torch.uint8), _dev(scales, "scales", torch.float32)
+    else:
+        r = s = ctypes.c_void_p(None)
+    with torch.cuda.device(out.device):
+        _check("sl_aggregate_interleaved", load().sl_aggregate_interleaved(r, s, ctypes.c_int32(N), o, ctypes.c_int64(n),
+                                                                           _stream_of(out, stream)))
 
 
 def sl_aggregate_apply(payloads, scales, theta: torch.Tensor, stream=None) -> None:

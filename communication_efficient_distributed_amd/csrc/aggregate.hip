@@ -361,6 +361,66 @@ __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, i
     }
 }
 
+// Records laid out chunk-major across peers (interleaved): chunk c's record
+// from peer p at records + (c * n_peers + p) * 112, its scale at
+// scales[c * n_peers + p].  A chunk's records are then one contiguous span, and
+// group g of nine peers is 63 consecutive 16-byte quads of it, so lane l reads
+// quad 63 g + l (peer 9 g + l / 7, bytes 16 (l % 7)) and lane q < 9 peer 9 g + q's
+// scale.  Lanes past the last peer (and lane 63) re-read peer 0's, as in
+// load_records.  The addresses are computed, so no per-lane pointer table is
+// held.
+template <int NGMAX>
+__device__ __forceinline__ void load_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                                 int64_t chunk, int lane, ChunkRecords<NGMAX>& cr) {
+    typedef const __attribute__((address_space(1))) float gfloat;
+    const int rp = lane / kQuads;
+    const int rq = lane - kQuads * rp;
+    const uint8_t* rbase = records + (size_t)chunk * (size_t)n_peers * SL_PAYLOAD_BYTES;
+    const float* sbase = scales + (size_t)chunk * (size_t)n_peers;
+#pragma unroll
+    for (int g = 0; g < NGMAX; ++g) {
+        const int p = kPeersPerLoad * g + rp;
+        const int quad = rp < kPeersPerLoad && p < n_peers ? kQuads * p + rq : rq;
+        const int ps = kPeersPerLoad * g + (lane < kPeersPerLoad ? lane : 0);
+        cr.r[g] = load_record16(rbase + 16 * (size_t)quad);
+        cr.sv[g] = *(gfloat*)(sbase + (ps < n_peers ? ps : 0));
+    }
+}
+
+// sl_aggregate_interleaved: CPW neighbouring chunks per wavefront from the
+// interleaved layout, the same sums in the same order as aggregate_kernel.
+template <int NGMAX, int CPW>
+__global__ __launch_bounds__(kWave) void aggregate_interleaved_kernel(const uint8_t* records, const float* scales,
+                                                                      int32_t n_peers, float* out, int64_t n_chunks,
+                                                                      int64_t per_xcd) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t c0 = CPW * xcd_chunk(per_xcd);
+    if (c0 >= n_chunks) return;
+    const int64_t count = n_chunks - c0 < CPW ? n_chunks - c0 : CPW;  // the same in every lane
+    ChunkRecords<NGMAX> cr[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
+        load_interleaved<NGMAX>(records, scales, n_peers, i < count ? c0 + i : c0, lane, cr[i]);
+    if constexpr (CPW == 1 && NGMAX >= 9) {
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(cr[0].r[g]));
+    }
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        if (i < count) {
+            sum_records<NGMAX>(cr[i], n_peers, tile, stage, lane);
+            if (i == 0) {
+#pragma unroll
+                for (int j = 1; j < CPW; ++j) await_records<NGMAX>(cr[j]);
+            }
+            wave_sync();
+            store_tile(tile, out + (size_t)(c0 + i) * SL_CHUNK, lane);
+        }
+    }
+}
+
 // The run kernel is used when a launch's records and scales exceed 224 MiB,
 // about what the 256 MB last-level cache keeps of them between calls: they
 // then come from HBM, and the later chunks' loads hide that latency.  Records
@@ -548,6 +608,32 @@ hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float*
     return hipSuccess;
 }
 
+// One chunk per wavefront except from 28 to 54 peers, where two measured
+// faster.  At 8192 x 28672 with records from HBM (two or four record sets
+// alternated), one / two / three chunks per wavefront, us:
+//   24 peers   198-199   202   211        36 peers   226   214   221
+//   48 peers   249       236   242        55 peers   235   246
+//   64 peers   245       261              81 peers   265   284
+//   128 peers  373       386              decoder block, 24 peers: 703 / 710 / 743
+// against, for the same records laid out per peer (sl_aggregate), 213-217,
+// 237-240, 272-274, 290-297, 310-319, 345-356, 492-512 and 760-770.  With
+// records in the last-level cache (24 peers, one set re-read) 161 / 166 / 173
+// against 152-157.
+hipError_t launch_interleaved_one(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
+                                  int64_t n_chunks, hipStream_t stream) {
+    const int R = n_peers > kPeersPerLoad * 3 && n_peers <= kRunMaxPeers ? 2 : 1;
+    const int64_t runs = (n_chunks + R - 1) / R;
+    int64_t per_xcd = (runs + kXcds - 1) / kXcds;
+    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&out, (void*)&n_chunks, (void*)&per_xcd};
+    const void* k = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<1, 1>)
+                    : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<2, 1>)
+                    : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<3, 1>)
+                    : n_peers <= kRunMaxPeers      ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<6, 2>)
+                    : n_peers <= kPairMaxPeers     ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<9, 1>)
+                                                   : reinterpret_cast<const void*>(&aggregate_interleaved_kernel<15, 1>);
+    return hipLaunchKernel(k, dim3((unsigned)(per_xcd * kXcds)), dim3(kWave), args, 0, stream);
+}
+
 }  // namespace
 
 hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
@@ -558,6 +644,18 @@ hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
 hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
                                   int64_t n_chunks, hipStream_t stream) {
     return launch_aggregate_impl<true>(peers, n_peers, theta, n_chunks, stream);
+}
+
+hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
+                                        int64_t n_chunks, hipStream_t stream) {
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
+        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+        const hipError_t e = launch_interleaved_one(records + (size_t)c0 * (size_t)n_peers * SL_PAYLOAD_BYTES,
+                                                    scales + (size_t)c0 * (size_t)n_peers, n_peers,
+                                                    out + (size_t)c0 * SL_CHUNK, m, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t n,

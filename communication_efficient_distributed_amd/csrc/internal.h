@@ -28,6 +28,12 @@ hipError_t launch_compress(const float* delta, float* ef, float beta, uint8_t* p
 hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
                             int64_t n_chunks, hipStream_t stream);
 
+// Records laid out chunk-major across peers: chunk c's record from peer p at
+// records + (c * n_peers + p) * 112, its scale at scales[c * n_peers + p];
+// n_peers >= 1.
+hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
+                                        int64_t n_chunks, hipStream_t stream);
+
 hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
                                   int64_t n_chunks, hipStream_t stream);
 

@@ -259,6 +259,29 @@ sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scale
                                          static_cast<hipStream_t>(stream)));
 }
 
+sl_status sl_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
+                                   int64_t n, void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n == 0) return SL_OK;
+    if (!out) return SL_ERR_INVALID_ARG;
+    if (!aligned(out, 16)) return SL_ERR_ALIGN;
+    const int64_t n_chunks = n / SL_CHUNK;
+    if (n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    if (n_peers == 0) {
+        const sl::PeerTable empty = {};
+        return from_hip(sl::launch_aggregate(empty, 0, out, n_chunks, static_cast<hipStream_t>(stream)));
+    }
+    if (!records || !scales) return SL_ERR_INVALID_ARG;
+    if (!aligned(records, 16) || !aligned(scales, 4)) return SL_ERR_ALIGN;
+    const size_t dense = (size_t)n * sizeof(float);
+    const size_t rbytes = (size_t)n_chunks * (size_t)n_peers * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * (size_t)n_peers * sizeof(float);
+    if (overlap(out, dense, records, rbytes) || overlap(out, dense, scales, sbytes)) return SL_ERR_INVALID_ARG;
+    return from_hip(sl::launch_aggregate_interleaved(records, scales, n_peers, out, n_chunks,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 sl_status sl_aggregate_apply(const uint8_t* const* payloads, const float* const* scales,
                              int32_t n_peers, float* theta, int64_t n, void* stream) {
     if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;

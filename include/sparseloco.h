@@ -155,6 +155,32 @@ sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t
                         void* stream);
 
 /*
+ * sl_aggregate_interleaved -- sl_aggregate with the peers' records laid out
+ * chunk-major across peers.
+ *
+ * Same sums as sl_aggregate, bit for bit, for the same records ([SF] "Why
+ * Extreme Sparsity Doesn't Break Convergence"; same reading).  Only the
+ * layout differs: chunk c's record from peer p is at records + (c * n_peers +
+ * p) * 112 and its scale at scales[c * n_peers + p], so every chunk's records
+ * are one contiguous span.  When the records come from HBM rather than the
+ * last-level cache, that span is served faster than n_peers separate record
+ * streams.  A receiver that uploads peers' records from host memory can write
+ * this layout directly: one 2-D copy per peer (hipMemcpy2DAsync, destination
+ * records + p * 112 with pitch n_peers * 112, source pitch 112, width 112,
+ * height n / 4096; scales likewise with 4-byte rows).
+ *
+ * records  in  DEVICE uint8[n/4096][n_peers][112], 16-byte aligned
+ * scales   in  DEVICE float32[n/4096][n_peers], 4-byte aligned
+ * n_peers  0..SL_MAX_PEERS (0 writes all +0.0 and reads neither input)
+ * out      out float32[n], 16-byte aligned, fully overwritten; must not overlap
+ *          records or scales
+ * n        number of parameters, a multiple of SL_CHUNK
+ * Payloads are trusted, as for sl_aggregate.
+ */
+sl_status sl_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                   float* out, int64_t n, void* stream);
+
+/*
  * sl_aggregate_apply -- sl_aggregate followed by sl_apply_mean without the dense
  * update ever reaching HBM.
  *

@@ -126,6 +126,27 @@ def test_aggregate_argument_checks(lib):
     assert lib.sl_aggregate(None, None, 2, O, N, None) == SL_ERR_INVALID_ARG
 
 
+def test_aggregate_interleaved_argument_checks(lib):
+    """Every call here is rejected (or is a no-op) on the host, before any
+    launch.  N = 16 chunks: records 3 x 16 x 112 bytes from R, scales from S."""
+    R = P
+    f = lib.sl_aggregate_interleaved
+    assert f(R, S, 3, O, 100, None) == SL_ERR_SHAPE
+    assert f(R, S, 3, O, -4096, None) == SL_ERR_SHAPE
+    assert f(R, S, -1, O, N, None) == SL_ERR_TOO_MANY_PEERS
+    assert f(R, S, 129, O, N, None) == SL_ERR_TOO_MANY_PEERS
+    assert f(R, S, 3, O, 0, None) == SL_OK                              # no-op
+    assert f(R, S, 3, None, N, None) == SL_ERR_INVALID_ARG
+    assert f(R, S, 3, O + 4, N, None) == SL_ERR_ALIGN
+    assert f(None, S, 3, O, N, None) == SL_ERR_INVALID_ARG
+    assert f(R, None, 3, O, N, None) == SL_ERR_INVALID_ARG
+    assert f(R + 8, S, 3, O, N, None) == SL_ERR_ALIGN
+    assert f(R, S + 2, 3, O, N, None) == SL_ERR_ALIGN
+    assert f(O + 4096, S, 3, O, N, None) == SL_ERR_INVALID_ARG          # records inside out
+    assert f(R, O + 64, 3, O, N, None) == SL_ERR_INVALID_ARG            # scales inside out
+    assert f(O - 3 * 16 * 112 + 16, S, 3, O, N, None) == SL_ERR_INVALID_ARG   # records reach out
+
+
 def test_apply_mean_argument_checks(lib):
     assert lib.sl_apply_mean(T, O, 24, 4097, None) == SL_ERR_SHAPE
     assert lib.sl_apply_mean(T, O, 0, N, None) == SL_ERR_TOO_MANY_PEERS

@@ -288,3 +288,99 @@ def test_records_beyond_cache(orc, n_peers):
     o = orc.aggregate(pay_o, sc_o, sample.size * 4096, nthreads=oracle_threads())
     assert_bitwise(g, o, f"aggregate beyond cache, {n_peers} peers")
     assert not torch.isnan(out).any().item(), "an output chunk was not written"
+
+
+# sl_aggregate_interleaved: the same records laid out chunk-major across peers
+# (record (c, p) at (c * n_peers + p) * 112).  The layout is built on the host
+# from the oracle's per-peer records; the oracle sums the per-peer lists.
+def interleave(payloads, scales, C):
+    rec = np.stack(payloads, axis=1) if payloads else np.zeros((C, 0, 112), np.uint8)
+    sc = np.stack(scales, axis=1) if scales else np.zeros((C, 0), np.float32)
+    return np.ascontiguousarray(rec), np.ascontiguousarray(sc)
+
+
+def gpu_aggregate_interleaved(sl, rec, sc, n):
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    sl.sl_aggregate_interleaved(torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda(), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+# Both ends of every variant (one chunk per wavefront up to 27 peers, two up to
+# 54, one up to 81 and beyond), 61 chunks so a two-chunk run is left partial.
+@pytest.mark.parametrize("n_peers", [0, 1, 9, 10, 18, 19, 24, 27, 28, 54, 55, 81, 82, 128])
+def test_interleaved_records(orc, n_peers):
+    sl = require_gpu()
+    C = 61
+    n = C * 4096
+    payloads, scales = random_peers(orc, n_peers, C, 700 + n_peers)
+    rec, sc = interleave(payloads, scales, C)
+    note(f"sl_aggregate_interleaved n_peers={n_peers} chunks={C}")
+    got = gpu_aggregate_interleaved(sl, rec, sc, n)
+    assert_bitwise(got, orc.aggregate(payloads, scales, n), f"interleaved, {n_peers} peers")
+
+
+# Records larger than the last-level cache, every variant; sampled chunks
+# (the first, the last three, 300 random) bitwise and every output written.
+@pytest.mark.parametrize("n_peers", [24, 48, 64, 128])
+def test_interleaved_records_beyond_cache(orc, n_peers):
+    sl = require_gpu()
+    C = (224 << 20) // (n_peers * 116) + 1001
+    n = C * 4096
+    idx, code, s0 = datagen.random_entries_bulk(C, seed=5000 + n_peers)
+    base = orc.pack(idx, code)
+    del idx, code
+    rng = np.random.default_rng(50 + n_peers)
+    sample = np.unique(np.r_[0, 1, 2, C - 3, C - 2, C - 1, rng.choice(C, 300, replace=False)])
+    rec = np.empty((C, n_peers, 112), np.uint8)
+    sc = np.empty((C, n_peers), np.float32)
+    pay_o, sc_o = [], []
+    for p in range(n_peers):
+        shift = (7919 * p + 13) % C
+        rec[:, p, :] = np.roll(base, shift, axis=0)
+        sc[:, p] = np.roll(s0, shift) * np.float32(1.0 + p / 8.0)
+        pay_o.append(rec[sample, p, :].copy())
+        sc_o.append(sc[sample, p].copy())
+    note(f"sl_aggregate_interleaved beyond the cache: n_peers={n_peers} chunks={C}")
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    sl.sl_aggregate_interleaved(torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda(), out)
+    torch.cuda.synchronize()
+    del rec, sc
+    i = torch.from_numpy(sample).cuda()
+    g = out.view(-1, 4096).index_select(0, i).cpu().numpy().reshape(-1)
+    o = orc.aggregate(pay_o, sc_o, sample.size * 4096, nthreads=oracle_threads())
+    assert_bitwise(g, o, f"interleaved beyond cache, {n_peers} peers")
+    assert not torch.isnan(out).any().item(), "an output chunk was not written"
+
+
+def test_interleaved_layout_from_host_by_2d_copies(orc):
+    """The upload the header describes: one hipMemcpy2DAsync per peer from its
+    pinned host records (pitch 112) into the chunk-major device buffer (pitch
+    n_peers * 112), scales likewise; then the same sums as sl_aggregate."""
+    import ctypes
+    sl = require_gpu()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy2DAsync.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    hip.hipMemcpy2DAsync.restype = ctypes.c_int
+    H2D = 1
+    N, C = 24, 300
+    n = C * 4096
+    payloads, scales = random_peers(orc, N, C, 777)
+    rec = torch.empty((C, N, 112), dtype=torch.uint8, device="cuda")
+    sc = torch.empty((C, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    host = []
+    for p in range(N):
+        hp = torch.from_numpy(payloads[p]).pin_memory()
+        hs = torch.from_numpy(scales[p]).pin_memory()
+        host += [hp, hs]
+        note(f"2-D upload of peer {p}")
+        assert hip.hipMemcpy2DAsync(rec.data_ptr() + 112 * p, N * 112, hp.data_ptr(), 112, 112, C, H2D,
+                                    stream.cuda_stream) == 0
+        assert hip.hipMemcpy2DAsync(sc.data_ptr() + 4 * p, N * 4, hs.data_ptr(), 4, 4, C, H2D,
+                                    stream.cuda_stream) == 0
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    sl.sl_aggregate_interleaved(rec, sc, out)
+    torch.cuda.synchronize()
+    assert_bitwise(out.cpu().numpy(), orc.aggregate(payloads, scales, n), "interleaved after 2-D uploads")

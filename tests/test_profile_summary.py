@@ -41,6 +41,11 @@ MEAN = "sl::(anonymous namespace)::apply_mean_kernel(float*, float const*, float
 RUN63 = "void sl::(anonymous namespace)::aggregate_run_kernel<6, 3>(sl::PeerTable, int, float*, long, long)"
 RUN151 = "void sl::(anonymous namespace)::aggregate_run_kernel<15, 1>(sl::PeerTable, int, float*, long, long)"
 RUN_ITEMS = ((C + 2) // 3 + 7) // 8 * 8 * 64
+IL31 = "void sl::(anonymous namespace)::aggregate_interleaved_kernel<3, 1>(unsigned char const*, float const*, int, " \
+       "float*, long, long)"
+IL62 = IL31.replace("<3, 1>", "<6, 2>")
+IL151 = IL31.replace("<3, 1>", "<15, 1>")
+IL2_ITEMS = ((C + 1) // 2 + 7) // 8 * 8 * 64
 COPY = "__amd_rocclr_copyBuffer"
 TORCH = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >(int, at::native::FillFunctor<float>, std::array<char*, 2ul>)"
 
@@ -55,19 +60,28 @@ SEQUENCE = (
     + [(COMPRESS, C * 256, 256, 8 * N / 2048, (4 + REC) * N / 1024, 451.0), (AGG, AGG_ITEMS, 64,
                                                                             P * REC * N / 2048, 4 * N / 1024,
                                                                             220.0)] * (S + K)
+    # the same cold steps with chunk-major records
+    + [(COMPRESS, C * 256, 256, 8 * N / 2048, (4 + REC) * N / 1024, 452.0), (IL31, AGG_ITEMS, 64,
+                                                                            P * REC * N / 2048, 4 * N / 1024,
+                                                                            199.0)] * (S + K)
     + [(MEAN, C * 256, 256, 8 * N / 2048, 4 * N / 1024, 430.0)] * (W + K)
     # the many-peer section: 36 peers (three chunks per wavefront), then 128 (one), 3 + 2 calls each
     + [(RUN63, RUN_ITEMS, 64, 36 * REC * N / 2048, 4 * N / 1024, 240.0)] * 5
     + [(RUN151, AGG_ITEMS, 64, 128 * REC * N / 2048, 4 * N / 1024, 500.0)] * 5
+    # then chunk-major: 36 peers (two chunks per wavefront), 128 (one)
+    + [(IL62, IL2_ITEMS, 64, 36 * REC * N / 2048, 4 * N / 1024, 215.0)] * 5
+    + [(IL151, AGG_ITEMS, 64, 128 * REC * N / 2048, 4 * N / 1024, 373.0)] * 5
 )
 
 
 def bench_line():
     return {"metric": bench.METRIC, "value": 350.0, "steps": K, "warmup": W, "ms_per_step": 0.67,
             "config": {"peers": P}, "roofline": {"bound": "hbm", "frac": 0.79},
-            "workloads": {"mlp_many_peers": {"params": N, "chunks": C, "36": {"ms": 0.24}, "128": {"ms": 0.56}}},
+            "workloads": {"mlp_many_peers": {"params": N, "chunks": C, "36": {"ms": 0.24}, "128": {"ms": 0.56},
+                                             "interleaved": {"36": {"ms": 0.215}, "128": {"ms": 0.373}}}},
             "kernels": {"compress": {"ms": 0.45}, "aggregate": {"ms": 0.152},
-                        "aggregate_cold": {"ms": 0.22, "record_sets": S}, "apply_mean": {"ms": 0.43}}}
+                        "aggregate_cold": {"ms": 0.22, "record_sets": S},
+                        "aggregate_cold_interleaved": {"ms": 0.199, "record_sets": S}, "apply_mean": {"ms": 0.43}}}
 
 
 def write_fixture(base):
@@ -116,9 +130,9 @@ def test_compress_summary_carries_calibrated_traffic_and_the_code_digest(summary
     assert "factor 2.0000" in txt and "factor 1.0000" in txt
     digest = re.search(r"compress_code_sha256_16:\s*([0-9a-f]{16})", txt).group(1)
     assert digest == bench.code_digest(bench.KERNEL_SOURCES)
-    # 96 setup + 4 step + 7 cold-step dispatches; the step ones read 1% more
-    assert "dispatches_sampled: 107" in txt
-    reads = (P * S * 1.0 + (W + K) * 1.01 + (S + K) * 1.0) / 107 * 8 * N
+    # 96 setup + 4 step + 7 cold-step + 7 chunk-major cold-step dispatches; the step ones read 1% more
+    assert "dispatches_sampled: 114" in txt
+    reads = (P * S * 1.0 + (W + K) * 1.01 + 2 * (S + K) * 1.0) / 114 * 8 * N
     writes = (4 + REC) * N
     got = float(re.search(r"compress_hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt).group(1))
     assert got == pytest.approx(reads + writes, rel=1e-5)
@@ -131,9 +145,10 @@ def test_compress_summary_carries_calibrated_traffic_and_the_code_digest(summary
 def test_aggregate_summary_separates_cache_resident_and_cold_calls(summary):
     out, _ = summary
     txt = (out / "aggregate_mlp_8192x28672_counters.txt").read_text()
-    warm, cold = txt.split("records from HBM")
+    warm, cold, chunk_major = txt.split("records from HBM")
     assert "dispatches_sampled: 4" in warm and "dispatches_sampled: 7" in cold
-    assert txt.count("ratio 1.000") == 4
+    assert "laid out chunk-major" in chunk_major and "dispatches_sampled: 7" in chunk_major
+    assert txt.count("ratio 1.000") == 6
     assert (out / "apply_mean_mlp_8192x28672_counters.txt").exists()
 
 
@@ -141,7 +156,9 @@ def test_many_peer_sections_take_the_timed_calls_of_each_count(summary):
     out, _ = summary
     txt = (out / "aggregate_beyond_cache_counters.txt").read_text()
     for label in ("[8192 x 28672, 36 peers: aggregate_run_kernel<6, 3>]",
-                  "[8192 x 28672, 128 peers: aggregate_run_kernel<15, 1>]"):
+                  "[8192 x 28672, 128 peers: aggregate_run_kernel<15, 1>]",
+                  "[8192 x 28672, 36 peers, chunk-major: aggregate_interleaved_kernel<6, 2>]",
+                  "[8192 x 28672, 128 peers, chunk-major: aggregate_interleaved_kernel<15, 1>]"):
         block = txt.split(label)[1].split("\n[")[0]
         assert "dispatches_sampled: 2" in block and "ratio 1.000" in block
 
@@ -163,7 +180,8 @@ def test_trace_summary_groups_dispatches_by_kernel_and_shape(summary):
     assert row("aggregate_kernel<3, false> [8192x28672, records cached]") == (W + K, 152.0)
     assert row("aggregate_kernel<3, false> [8192x28672, records from HBM]") == (S + K, 220.0)
     calls, avg = row("compress_kernel<false> [8192x28672]")
-    assert calls == P * S + W + K + S + K
+    assert calls == P * S + W + K + 2 * (S + K)
+    assert row("aggregate_interleaved_kernel<3, 1> [8192x28672, records from HBM, chunk-major]") == (S + K, 199.0)
     assert row("compress_kernel<false> [8192x28672, timed steps only]") == (K, 449.0)
     assert row("step aggregate [8192x28672, records cached, timed steps only]") == (K, 152.0)
 
