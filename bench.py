@@ -594,13 +594,28 @@ def workloads(sl, dev, shapes, done=lambda what: None, reps=10):
             t, ts = timed_calls(torch, stream, cold_il_call, k=reps)
             r["aggregate_cold_interleaved"] = dict(st(n, t, BYTES_AGGREGATE, ts), record_sets=2,
                                                    note="the same two sets laid out chunk-major across peers")
-            del sets, pp2, ps2, il
             datagen.fill_lognormal_(a, W, 0, 0)
             ef.zero_()
             theta = ef
             theta.copy_(a).mul_(0.02)
             t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate_apply(peers, None, theta), k=reps)
             r["aggregate_apply_fused"] = st(n, t, 8 + N_PEERS * RECORD / CHUNK, ts)
+
+            def fused_cold():
+                turn[0] += 1
+                sl.sl_aggregate_apply(sets[turn[0] % 2], None, theta)
+
+            def fused_cold_il():
+                turn[0] += 1
+                r_, s_ = il[turn[0] % 2]
+                sl.sl_aggregate_apply_interleaved(r_, s_, theta)
+
+            t, ts = timed_calls(torch, stream, fused_cold, k=reps)
+            r["aggregate_apply_fused_cold"] = dict(st(n, t, 8 + N_PEERS * RECORD / CHUNK, ts), record_sets=2)
+            t, ts = timed_calls(torch, stream, fused_cold_il, k=reps)
+            r["aggregate_apply_fused_cold_interleaved"] = dict(st(n, t, 8 + N_PEERS * RECORD / CHUNK, ts),
+                                                               record_sets=2)
+            del sets, pp2, ps2, il
             t, ts = timed_calls(torch, stream, lambda: sl.sl_apply_mean(theta, out, N_PEERS), k=reps)
             r["apply_mean"] = st(n, t, BYTES_APPLY, ts)
         res[name] = r

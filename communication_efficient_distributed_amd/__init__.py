@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     load,
     sl_aggregate,
     sl_aggregate_apply,
+    sl_aggregate_apply_interleaved,
     sl_aggregate_interleaved,
     sl_apply_mean,
     sl_compress,

@@ -29,6 +29,7 @@ STATUS = {
 }
 
 EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_interleaved", "sl_aggregate_apply",
+           "sl_aggregate_apply_interleaved",
            "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_peer_stats",
            "sl_peer_stats_noalloc", "sl_host_device_pointer", "sl_status_string")
 
@@ -75,6 +76,8 @@ def load():
     L.sl_aggregate.restype = ctypes.c_int
     L.sl_aggregate_interleaved.argtypes = [P, P, I32, P, I64, P]
     L.sl_aggregate_interleaved.restype = ctypes.c_int
+    L.sl_aggregate_apply_interleaved.argtypes = [P, P, I32, P, I64, P]
+    L.sl_aggregate_apply_interleaved.restype = ctypes.c_int
     L.sl_aggregate_apply.argtypes = [P, P, I32, P, I64, P]
     L.sl_aggregate_apply.restype = ctypes.c_int
     L.sl_apply_mean.argtypes = [P, P, I32, I64, P]
@@ -321,6 +324,27 @@ def sl_aggregate_interleaved(records: torch.Tensor, scales: torch.Tensor, out: t
     with torch.cuda.device(out.device):
         _check("sl_aggregate_interleaved", load().sl_aggregate_interleaved(r, s, ctypes.c_int32(N), o, ctypes.c_int64(n),
                                                                            _stream_of(out, stream)))
+
+
+def sl_aggregate_apply_interleaved(records: torch.Tensor, scales: torch.Tensor, theta: torch.Tensor,
+                                   stream=None) -> None:
+    """sl_aggregate_apply on records laid out chunk-major across peers (records
+    uint8 [n/4096, n_peers, 112], scales float32 [n/4096, n_peers]): theta <-
+    theta - sum / n_peers in one pass."""
+    if records.dim() != 3 or records.shape[2] != SL_PAYLOAD_BYTES:
+        raise ValueError("records must be a [n_chunks, n_peers, 112] tensor")
+    C, N = records.shape[0], records.shape[1]
+    if scales.dim() != 2 or tuple(scales.shape) != (C, N):
+        raise ValueError("scales must be a [n_chunks, n_peers] tensor")
+    n = theta.numel()
+    if n != C * SL_CHUNK:
+        raise ValueError("theta must hold n_chunks * 4096 floats")
+    t = _dev(theta, "theta", torch.float32)
+    r, s = _dev(records, "records", torch.uint8), _dev(scales, "scales", torch.float32)
+    with torch.cuda.device(theta.device):
+        _check("sl_aggregate_apply_interleaved",
+               load().sl_aggregate_apply_interleaved(r, s, ctypes.c_int32(N), t, ctypes.c_int64(n),
+                                                     _stream_of(theta, stream)))
 
 
 def sl_aggregate_apply(payloads, scales, theta: torch.Tensor, stream=None) -> None:

@@ -493,6 +493,78 @@ __global__ __launch_bounds__(kWave * kApplyWaves) void aggregate_apply4_kernel(P
     }
 }
 
+// The fused update on interleaved records: the same operations as
+// aggregate_apply4_kernel (up to 27 peers) and aggregate_kernel<NGMAX, true>
+// (beyond), with the records loaded by load_interleaved.
+template <int NGMAX>
+__global__ __launch_bounds__(kWave * kApplyWaves) void apply4_interleaved_kernel(const uint8_t* records,
+                                                                                 const float* scales, int32_t n_peers,
+                                                                                 float* theta, int64_t n_chunks,
+                                                                                 int64_t per_xcd, float nf) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t chunk = xcd_chunk(per_xcd);
+    if (chunk >= n_chunks) return;  // the whole workgroup
+    float* th_chunk = theta + (size_t)chunk * SL_CHUNK;
+    v4f th[kQuarterSlots];
+    auto load_quarter = [&] {
+#pragma unroll
+        for (int m = 0; m < kQuarterSlots; ++m)
+            th[m] = __builtin_nontemporal_load(
+                reinterpret_cast<const v4f*>(th_chunk + 4 * ((kQuarterSlots * w + m) * kWave + lane)));
+    };
+    if (w == 0) {
+        ChunkRecords<NGMAX> cr;
+        load_interleaved<NGMAX>(records, scales, n_peers, chunk, lane, cr);
+        load_quarter();
+        sum_records<NGMAX>(cr, n_peers, tile, stage, lane);
+    } else {
+        load_quarter();
+    }
+    __syncthreads();
+    const float4* t4 = reinterpret_cast<const float4*>(tile);
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(th_chunk);
+#pragma unroll
+    for (int m = 0; m < kQuarterSlots; ++m) {
+        const int slot = kQuarterSlots * w + m;
+        const float4 o = t4[slot * kWave + lane];
+        v4f r;
+        r.x = th[m].x - o.x / nf;
+        r.y = th[m].y - o.y / nf;
+        r.z = th[m].z - o.z / nf;
+        r.w = th[m].w - o.w / nf;
+        store_slot<kStorePolicy>(rs, slot, lane, r);
+    }
+}
+
+template <int NGMAX>
+__global__ __launch_bounds__(kWave) void apply_interleaved_kernel(const uint8_t* records, const float* scales,
+                                                                  int32_t n_peers, float* theta, int64_t n_chunks,
+                                                                  int64_t per_xcd, float nf) {
+    __shared__ __align__(16) float tile[SL_CHUNK];
+    __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
+    const int lane = (int)threadIdx.x;
+    const int64_t chunk = xcd_chunk(per_xcd);
+    if (chunk >= n_chunks) return;
+    float* th_chunk = theta + (size_t)chunk * SL_CHUNK;
+    ChunkRecords<NGMAX> cr;
+    load_interleaved<NGMAX>(records, scales, n_peers, chunk, lane, cr);
+    if constexpr (NGMAX >= 9) {
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g) asm volatile("" ::"v"(cr.r[g]));
+    }
+    constexpr bool kEarlyTheta = NGMAX <= 9;
+    v4f th[kSlots];
+    if constexpr (kEarlyTheta) load_theta<true>(th_chunk, th, lane);
+    sum_records<NGMAX>(cr, n_peers, tile, stage, lane);
+    if constexpr (!kEarlyTheta) load_theta<true>(th_chunk, th, lane);
+    wave_sync();
+    finish_chunk<true>(tile, th_chunk, th, nf, lane);
+}
+
 // theta <- theta - out / n_peers.  One workgroup of four wavefronts per
 // 4096-element chunk; wavefront w streams its own contiguous quarter (four
 // float4 of each stream per lane, 1 KiB per instruction), nontemporal loads
@@ -646,6 +718,29 @@ hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float
     return launch_aggregate_impl<true>(peers, n_peers, theta, n_chunks, stream);
 }
 
+// Fused update on interleaved records, with the same workgroup shapes and
+// residency caps as the per-peer layout's fused update.
+hipError_t launch_apply_interleaved_one(const uint8_t* records, const float* scales, int32_t n_peers, float* theta,
+                                        int64_t n_chunks, hipStream_t stream) {
+    float nf = (float)n_peers;
+    int64_t per_xcd = (n_chunks + kXcds - 1) / kXcds;
+    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&theta, (void*)&n_chunks,
+                    (void*)&per_xcd, (void*)&nf};
+    const dim3 grid((unsigned)(per_xcd * kXcds));
+    if (n_peers <= kPeersPerLoad * 3) {
+        constexpr size_t kStatic = sizeof(float) * SL_CHUNK + sizeof(uint32_t) * (kPeersPerLoad + 1) * kRecWords;
+        const void* k4 = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&apply4_interleaved_kernel<1>)
+                         : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&apply4_interleaved_kernel<2>)
+                                                        : reinterpret_cast<const void*>(&apply4_interleaved_kernel<3>);
+        const int cap = n_peers <= kPeersPerLoad * 2 ? 5 : 7;
+        return hipLaunchKernel(k4, grid, dim3(kWave * kApplyWaves), args, residency_lds(cap, kStatic), stream);
+    }
+    const void* k = n_peers <= kRunMaxPeers    ? reinterpret_cast<const void*>(&apply_interleaved_kernel<6>)
+                    : n_peers <= kPairMaxPeers ? reinterpret_cast<const void*>(&apply_interleaved_kernel<9>)
+                                               : reinterpret_cast<const void*>(&apply_interleaved_kernel<15>);
+    return hipLaunchKernel(k, grid, dim3(kWave), args, 0, stream);
+}
+
 hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
                                         int64_t n_chunks, hipStream_t stream) {
     for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
@@ -653,6 +748,18 @@ hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* sca
         const hipError_t e = launch_interleaved_one(records + (size_t)c0 * (size_t)n_peers * SL_PAYLOAD_BYTES,
                                                     scales + (size_t)c0 * (size_t)n_peers, n_peers,
                                                     out + (size_t)c0 * SL_CHUNK, m, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_aggregate_apply_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                              float* theta, int64_t n_chunks, hipStream_t stream) {
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
+        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+        const hipError_t e = launch_apply_interleaved_one(records + (size_t)c0 * (size_t)n_peers * SL_PAYLOAD_BYTES,
+                                                          scales + (size_t)c0 * (size_t)n_peers, n_peers,
+                                                          theta + (size_t)c0 * SL_CHUNK, m, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

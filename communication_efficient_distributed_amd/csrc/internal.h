@@ -34,6 +34,11 @@ hipError_t launch_aggregate(const PeerTable& peers, int32_t n_peers, float* out,
 hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
                                         int64_t n_chunks, hipStream_t stream);
 
+// The fused update theta <- theta - sum / n_peers on interleaved records
+// (n_peers >= 1).
+hipError_t launch_aggregate_apply_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                              float* theta, int64_t n_chunks, hipStream_t stream);
+
 hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float* theta,
                                   int64_t n_chunks, hipStream_t stream);
 

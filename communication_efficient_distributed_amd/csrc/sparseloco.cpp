@@ -282,6 +282,23 @@ sl_status sl_aggregate_interleaved(const uint8_t* records, const float* scales, 
                                                      static_cast<hipStream_t>(stream)));
 }
 
+sl_status sl_aggregate_apply_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                         float* theta, int64_t n, void* stream) {
+    if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;
+    if (n_peers < 1 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n == 0) return SL_OK;
+    if (!theta || !records || !scales) return SL_ERR_INVALID_ARG;
+    if (!aligned(theta, 16) || !aligned(records, 16) || !aligned(scales, 4)) return SL_ERR_ALIGN;
+    const int64_t n_chunks = n / SL_CHUNK;
+    if (n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    const size_t dense = (size_t)n * sizeof(float);
+    const size_t rbytes = (size_t)n_chunks * (size_t)n_peers * SL_PAYLOAD_BYTES;
+    const size_t sbytes = (size_t)n_chunks * (size_t)n_peers * sizeof(float);
+    if (overlap(theta, dense, records, rbytes) || overlap(theta, dense, scales, sbytes)) return SL_ERR_INVALID_ARG;
+    return from_hip(sl::launch_aggregate_apply_interleaved(records, scales, n_peers, theta, n_chunks,
+                                                           static_cast<hipStream_t>(stream)));
+}
+
 sl_status sl_aggregate_apply(const uint8_t* const* payloads, const float* const* scales,
                              int32_t n_peers, float* theta, int64_t n, void* stream) {
     if (n < 0 || n % SL_CHUNK != 0) return SL_ERR_SHAPE;

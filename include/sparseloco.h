@@ -139,6 +139,22 @@ sl_status sl_aggregate(const uint8_t* const* payloads, const float* const* scale
                        int32_t n_peers, float* out, int64_t n, void* stream);
 
 /*
+ * sl_aggregate_apply_interleaved -- sl_aggregate_apply with the records laid
+ * out chunk-major across peers, as for sl_aggregate_interleaved.
+ *
+ * Same reading and the same results, bit for bit, as sl_aggregate_apply on
+ * the per-peer buffers: theta[i] <- theta[i] - out[i] / n_peers.
+ *
+ * records, scales  as for sl_aggregate_interleaved
+ * n_peers  1..SL_MAX_PEERS, else SL_ERR_TOO_MANY_PEERS
+ * theta    in/out float32[n], 16-byte aligned; must not overlap records or
+ *          scales
+ * n        number of parameters, a multiple of SL_CHUNK
+ */
+sl_status sl_aggregate_apply_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                         float* theta, int64_t n, void* stream);
+
+/*
  * sl_apply_mean -- outer update with the aggregated sum.
  *
  * The pages do not describe the outer optimizer.  Reading: the pseudo-gradient

@@ -147,6 +147,23 @@ def test_aggregate_interleaved_argument_checks(lib):
     assert f(O - 3 * 16 * 112 + 16, S, 3, O, N, None) == SL_ERR_INVALID_ARG   # records reach out
 
 
+def test_aggregate_apply_interleaved_argument_checks(lib):
+    """Rejected on the host before any launch (theta at T, records at P, scales at S)."""
+    f = lib.sl_aggregate_apply_interleaved
+    assert f(P, S, 3, T, 100, None) == SL_ERR_SHAPE
+    assert f(P, S, 0, T, N, None) == SL_ERR_TOO_MANY_PEERS
+    assert f(P, S, 129, T, N, None) == SL_ERR_TOO_MANY_PEERS
+    assert f(P, S, 3, T, 0, None) == SL_OK                              # no-op
+    assert f(P, S, 3, None, N, None) == SL_ERR_INVALID_ARG
+    assert f(None, S, 3, T, N, None) == SL_ERR_INVALID_ARG
+    assert f(P, None, 3, T, N, None) == SL_ERR_INVALID_ARG
+    assert f(P, S, 3, T + 4, N, None) == SL_ERR_ALIGN
+    assert f(P + 8, S, 3, T, N, None) == SL_ERR_ALIGN
+    assert f(P, S + 2, 3, T, N, None) == SL_ERR_ALIGN
+    assert f(T + 4096, S, 3, T, N, None) == SL_ERR_INVALID_ARG          # records inside theta
+    assert f(P, T + 64, 3, T, N, None) == SL_ERR_INVALID_ARG            # scales inside theta
+
+
 def test_apply_mean_argument_checks(lib):
     assert lib.sl_apply_mean(T, O, 24, 4097, None) == SL_ERR_SHAPE
     assert lib.sl_apply_mean(T, O, 0, N, None) == SL_ERR_TOO_MANY_PEERS

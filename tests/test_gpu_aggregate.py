@@ -384,3 +384,21 @@ def test_interleaved_layout_from_host_by_2d_copies(orc):
     sl.sl_aggregate_interleaved(rec, sc, out)
     torch.cuda.synchronize()
     assert_bitwise(out.cpu().numpy(), orc.aggregate(payloads, scales, n), "interleaved after 2-D uploads")
+
+
+# sl_aggregate_apply_interleaved: both ends of every variant of the fused
+# update, against the oracle's aggregate then apply_mean on the per-peer lists.
+@pytest.mark.parametrize("n_peers,C", [(1, 61), (9, 61), (10, 61), (18, 61), (19, 61), (27, 61), (28, 61),
+                                       (54, 61), (55, 61), (81, 61), (82, 61), (128, 61), (24, 3001), (64, 1001)])
+def test_interleaved_fused_update(orc, n_peers, C):
+    sl = require_gpu()
+    n = C * 4096
+    payloads, scales = random_peers(orc, n_peers, C, 900 + n_peers)
+    rec, sc = interleave(payloads, scales, C)
+    theta0 = datagen.theta0(n, datagen.SMALL_1M).numpy()
+    theta = torch.from_numpy(theta0.copy()).cuda()
+    note(f"sl_aggregate_apply_interleaved n_peers={n_peers} chunks={C}")
+    sl.sl_aggregate_apply_interleaved(torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda(), theta)
+    torch.cuda.synchronize()
+    want = orc.apply_mean(theta0, orc.aggregate(payloads, scales, n, nthreads=oracle_threads()), n_peers)
+    assert_bitwise(theta.cpu().numpy(), want, f"fused interleaved, {n_peers} peers")
