@@ -402,3 +402,43 @@ def test_interleaved_fused_update(orc, n_peers, C):
     torch.cuda.synchronize()
     want = orc.apply_mean(theta0, orc.aggregate(payloads, scales, n, nthreads=oracle_threads()), n_peers)
     assert_bitwise(theta.cpu().numpy(), want, f"fused interleaved, {n_peers} peers")
+
+
+def test_interleaved_overlapping_indices_and_extreme_scales(orc):
+    """Chunk-major layout: all peers on the same 64 indices (0 and 4095 among
+    them) with scales from denormal to 1e30, and three peers whose scales cover
+    every fp32 binade; both the sums and the fused update, bitwise."""
+    sl = require_gpu()
+    C, N = 8, 24
+    idx = np.sort(np.r_[0, 4095, np.random.default_rng(11).choice(np.arange(1, 4095), 62, replace=False)])
+    rng = np.random.default_rng(12)
+    payloads, scales = [], []
+    for p in range(N):
+        cc = rng.integers(0, 4, (C, 64)).astype(np.uint8)
+        payloads.append(orc.pack(np.tile(idx, (C, 1)).astype(np.int32), cc))
+        scales.append(rng.choice(np.array([1e-42, 1e-30, 0.0, 1.0, 3.0, 1e30], np.float32), C).astype(np.float32))
+    n = C * 4096
+    rec, sc = interleave(payloads, scales, C)
+    note("sl_aggregate_interleaved overlapping indices")
+    assert_bitwise(gpu_aggregate_interleaved(sl, rec, sc, n), orc.aggregate(payloads, scales, n),
+                   "interleaved overlapping")
+
+    C = 1 << 14
+    payloads, scales = [], []
+    for p in range(3):
+        ii, cc, _ = datagen.random_entries_bulk(C, 4300 + p)
+        bits_ = np.random.default_rng(4310 + p).integers(0, 0x7F800000, C, dtype=np.uint32)
+        bits_[:4] = [0, 1, 0x007FFFFF, 0x7F7FFFFF]
+        payloads.append(orc.pack(ii, cc))
+        scales.append(bits_.view(np.float32))
+    n = C * 4096
+    rec, sc = interleave(payloads, scales, C)
+    note("sl_aggregate_interleaved scales over every binade")
+    want = orc.aggregate(payloads, scales, n, nthreads=oracle_threads())
+    assert_bitwise(gpu_aggregate_interleaved(sl, rec, sc, n), want, "interleaved over all binades")
+    theta0 = datagen.theta0(n, datagen.SMALL_1M).numpy()
+    theta = torch.from_numpy(theta0.copy()).cuda()
+    note("sl_aggregate_apply_interleaved scales over every binade")
+    sl.sl_aggregate_apply_interleaved(torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda(), theta)
+    torch.cuda.synchronize()
+    assert_bitwise(theta.cpu().numpy(), orc.apply_mean(theta0, want, 3), "fused interleaved over all binades")
