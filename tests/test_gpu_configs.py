@@ -223,14 +223,15 @@ def test_span_split_over_launches_sampled(orc):
     """A span of 2^22 + 3 chunks (17.2e9 parameters), one chunk past where the
     library splits a call into several kernel launches: compress (two rounds),
     compress from weights, 2-peer aggregate, fused aggregate-apply and
-    apply_mean, compared with the oracle on sampled chunks that include both
-    sides of the split."""
+    apply_mean, then the aggregate and the fused update on the same records laid
+    out chunk-major, compared with the oracle on sampled chunks that include
+    both sides of the split."""
     sl = require_gpu()
     W = datagen.FLAT_16B
     K = 1 << 22
     C = K + 3
     n = C * CHUNK
-    need = 2 * 4 * n + 3 * C * 116 + (8 << 30)   # two dense buffers, records, slack
+    need = 2 * 4 * n + 5 * C * 116 + (8 << 30)   # two dense buffers, records (both layouts), slack
     if _free_gpu_bytes() < need:
         pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory")
     T = oracle_threads()
@@ -298,3 +299,22 @@ def test_span_split_over_launches_sampled(orc):
     sl.sl_apply_mean(theta, out, 2)
     torch.cuda.synchronize()
     assert_bitwise(gather(theta, idx).reshape(-1), orc.apply_mean(th1, o, 2), "split apply_mean")
+
+    # The same two peers' records laid out chunk-major: each launch of the
+    # split must start at its own chunk's records (offset c0 * 2 * 112).
+    rec = torch.empty((C, 2, 112), dtype=torch.uint8, device=dev)
+    sc = torch.empty((C, 2), dtype=torch.float32, device=dev)
+    for k in range(2):
+        rec[:, k, :] = peer_p[k]
+        sc[:, k] = peer_s[k]
+    del peer_p, peer_s
+    note("split span: sl_aggregate_interleaved 2 peers")
+    out.fill_(float("nan"))
+    sl.sl_aggregate_interleaved(rec, sc, out)
+    torch.cuda.synchronize()
+    assert_bitwise(gather(out, idx).reshape(-1), o, "split aggregate, chunk-major")
+    datagen.fill_lognormal_(theta, W, 0, 0x103)
+    note("split span: sl_aggregate_apply_interleaved 2 peers")
+    sl.sl_aggregate_apply_interleaved(rec, sc, theta)
+    torch.cuda.synchronize()
+    assert_bitwise(gather(theta, idx).reshape(-1), th1, "split aggregate_apply, chunk-major")
