@@ -389,14 +389,22 @@ __device__ __forceinline__ void load_interleaved(const uint8_t* records, const f
 
 // sl_aggregate_interleaved: CPW neighbouring chunks per wavefront from the
 // interleaved layout, the same sums in the same order as aggregate_kernel.
+// Workgroup b takes run b: consecutive workgroups, which the dispatcher deals
+// round-robin over the XCDs, take neighbouring chunks, so the whole device
+// reads and writes one front of contiguous memory.  (The per-peer layout keeps
+// each XCD on a contiguous range instead, since its neighbouring records share
+// cache lines; here only one line per chunk span is shared.)  At 8192 x 28672
+// with records from HBM the linear order measured 189 / 221 / 229 / 250 / 343
+// us at 24 / 48 / 64 / 81 / 128 peers against 198 / 238 / 251 / 268 / 387 us
+// with the XCD ranges, and 686 against 704 us at the decoder block; the same
+// with records cached (162-163 against 162-165 us).
 template <int NGMAX, int CPW>
 __global__ __launch_bounds__(kWave) void aggregate_interleaved_kernel(const uint8_t* records, const float* scales,
-                                                                      int32_t n_peers, float* out, int64_t n_chunks,
-                                                                      int64_t per_xcd) {
+                                                                      int32_t n_peers, float* out, int64_t n_chunks) {
     __shared__ __align__(16) float tile[SL_CHUNK];
     __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
     const int lane = (int)threadIdx.x;
-    const int64_t c0 = CPW * xcd_chunk(per_xcd);
+    const int64_t c0 = CPW * (int64_t)blockIdx.x;
     if (c0 >= n_chunks) return;
     const int64_t count = n_chunks - c0 < CPW ? n_chunks - c0 : CPW;  // the same in every lane
     ChunkRecords<NGMAX> cr[CPW];
@@ -500,13 +508,13 @@ template <int NGMAX>
 __global__ __launch_bounds__(kWave * kApplyWaves) void apply4_interleaved_kernel(const uint8_t* records,
                                                                                  const float* scales, int32_t n_peers,
                                                                                  float* theta, int64_t n_chunks,
-                                                                                 int64_t per_xcd, float nf) {
+                                                                                 float nf) {
     __shared__ __align__(16) float tile[SL_CHUNK];
     __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
     const int tid = (int)threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t chunk = xcd_chunk(per_xcd);
+    const int64_t chunk = (int64_t)blockIdx.x;  // linear order, as the interleaved aggregate
     if (chunk >= n_chunks) return;  // the whole workgroup
     float* th_chunk = theta + (size_t)chunk * SL_CHUNK;
     v4f th[kQuarterSlots];
@@ -543,11 +551,11 @@ __global__ __launch_bounds__(kWave * kApplyWaves) void apply4_interleaved_kernel
 template <int NGMAX>
 __global__ __launch_bounds__(kWave) void apply_interleaved_kernel(const uint8_t* records, const float* scales,
                                                                   int32_t n_peers, float* theta, int64_t n_chunks,
-                                                                  int64_t per_xcd, float nf) {
+                                                                  float nf) {
     __shared__ __align__(16) float tile[SL_CHUNK];
     __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
     const int lane = (int)threadIdx.x;
-    const int64_t chunk = xcd_chunk(per_xcd);
+    const int64_t chunk = (int64_t)blockIdx.x;  // linear order, as the interleaved aggregate
     if (chunk >= n_chunks) return;
     float* th_chunk = theta + (size_t)chunk * SL_CHUNK;
     ChunkRecords<NGMAX> cr;
@@ -682,28 +690,24 @@ hipError_t launch_aggregate_impl(const PeerTable& peers, int32_t n_peers, float*
 
 // One chunk per wavefront except from 28 to 54 peers, where two measured
 // faster.  At 8192 x 28672 with records from HBM (two or four record sets
-// alternated), one / two / three chunks per wavefront, us:
-//   24 peers   198-199   202   211        36 peers   226   214   221
-//   48 peers   249       236   242        55 peers   235   246
-//   64 peers   245       261              81 peers   265   284
-//   128 peers  373       386              decoder block, 24 peers: 703 / 710 / 743
+// alternated), in the linear order, one / two chunks per wavefront, us:
+//   24 peers   189   201        36 peers   216   212        48 peers   241   221
+//   55 peers   231   226        64 peers   229   244        81 peers   250   267
+//   128 peers  343   363        decoder block, 24 peers: 686 / 731
 // against, for the same records laid out per peer (sl_aggregate), 213-217,
-// 237-240, 272-274, 290-297, 310-319, 345-356, 492-512 and 760-770.  With
-// records in the last-level cache (24 peers, one set re-read) 161 / 166 / 173
-// against 152-157.
+// 237-240, 257-274, 267-297, 285-319, 318-356, 471-512 and 760-770.
 hipError_t launch_interleaved_one(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
                                   int64_t n_chunks, hipStream_t stream) {
     const int R = n_peers > kPeersPerLoad * 3 && n_peers <= kRunMaxPeers ? 2 : 1;
     const int64_t runs = (n_chunks + R - 1) / R;
-    int64_t per_xcd = (runs + kXcds - 1) / kXcds;
-    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&out, (void*)&n_chunks, (void*)&per_xcd};
+    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&out, (void*)&n_chunks};
     const void* k = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<1, 1>)
                     : n_peers <= kPeersPerLoad * 2 ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<2, 1>)
                     : n_peers <= kPeersPerLoad * 3 ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<3, 1>)
                     : n_peers <= kRunMaxPeers      ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<6, 2>)
                     : n_peers <= kPairMaxPeers     ? reinterpret_cast<const void*>(&aggregate_interleaved_kernel<9, 1>)
                                                    : reinterpret_cast<const void*>(&aggregate_interleaved_kernel<15, 1>);
-    return hipLaunchKernel(k, dim3((unsigned)(per_xcd * kXcds)), dim3(kWave), args, 0, stream);
+    return hipLaunchKernel(k, dim3((unsigned)runs), dim3(kWave), args, 0, stream);
 }
 
 }  // namespace
@@ -723,10 +727,8 @@ hipError_t launch_aggregate_apply(const PeerTable& peers, int32_t n_peers, float
 hipError_t launch_apply_interleaved_one(const uint8_t* records, const float* scales, int32_t n_peers, float* theta,
                                         int64_t n_chunks, hipStream_t stream) {
     float nf = (float)n_peers;
-    int64_t per_xcd = (n_chunks + kXcds - 1) / kXcds;
-    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&theta, (void*)&n_chunks,
-                    (void*)&per_xcd, (void*)&nf};
-    const dim3 grid((unsigned)(per_xcd * kXcds));
+    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&theta, (void*)&n_chunks, (void*)&nf};
+    const dim3 grid((unsigned)n_chunks);
     if (n_peers <= kPeersPerLoad * 3) {
         constexpr size_t kStatic = sizeof(float) * SL_CHUNK + sizeof(uint32_t) * (kPeersPerLoad + 1) * kRecWords;
         const void* k4 = n_peers <= kPeersPerLoad * 1 ? reinterpret_cast<const void*>(&apply4_interleaved_kernel<1>)
