@@ -562,6 +562,15 @@ def workloads(sl, dev, shapes, done=lambda what: None, reps=10):
         r["compress"] = st(n, t, BYTES_COMPRESS, ts)
         t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate(peers, None, out), k=reps)
         r["aggregate"] = st(n, t, BYTES_AGGREGATE, ts)
+        if W == datagen.FLAT_16B:
+            # The same records laid out chunk-major, when the device has room
+            # for a second copy of them (10.9 GB).
+            free, _ = torch.cuda.mem_get_info(dev)
+            if free > N_PEERS * C * RECORD + (2 << 30):
+                il_r, il_s = interleaved_records(torch, pp, ps)
+                t, ts = timed_calls(torch, stream, lambda: sl.sl_aggregate_interleaved(il_r, il_s, out), k=reps)
+                r["aggregate_interleaved"] = st(n, t, BYTES_AGGREGATE, ts)
+                del il_r, il_s
         if W == datagen.DECODER_BLOCK:
             # One 581 MB record set read call after call stays partly in the
             # 256 MB last-level cache; a second set, alternated with the first,
