@@ -309,3 +309,83 @@ def test_outer_loop_rounds(orc):
             assert counts[p].cpu().tolist() == wc.tolist(), f"round {rnd} peer {p} counts"
             assert wc[0] == 0                         # the compressor's records are well formed
         assert_bitwise(theta_g.cpu().numpy(), theta_o, f"round {rnd} theta")
+
+
+def test_rounds_with_changing_participation_and_ef_resume(orc):
+    """Five outer rounds in which participation changes, as the pages' open
+    network allows: a peer that sits a round out runs no compressor, so its
+    error feedback is untouched; a peer whose records do not arrive (lost, or
+    filtered out by the validator) has still updated its own error feedback,
+    but the update sums only what arrived. The third round delivers nothing:
+    the sum is +0 everywhere and theta is left as it is. Before the fourth
+    round every peer's error feedback is saved to host memory, the device
+    buffers are freed, and the run continues from fresh buffers restored from
+    the saved copies; the error feedback is the compressor's only state, so
+    the continuation must match the oracle, which never stopped, bit for bit.
+    The last two rounds deliver chunk-major records (one peer, then all),
+    applied through sl_aggregate_apply_interleaved and through
+    sl_aggregate_interleaved + sl_apply_mean."""
+    sl = require_gpu()
+    N, C = 6, 37
+    n = C * 4096
+    W = datagen.SMALL_1M
+    # (peers that compress, peers whose records arrive) per round
+    rounds = [(range(6), range(6)),
+              ((0, 1, 2, 4, 5), (0, 2, 5)),
+              ((1, 3), ()),
+              (range(6), (3,)),
+              (range(6), range(6))]
+    theta_o = datagen.theta0(n, W).numpy()
+    theta_g = torch.from_numpy(theta_o).cuda()
+    ef_o = [np.zeros(n, np.float32) for _ in range(N)]
+    ef_g = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(N)]
+    pay_g = [torch.empty((C, 112), dtype=torch.uint8, device="cuda") for _ in range(N)]
+    sc_g = [torch.empty(C, dtype=torch.float32, device="cuda") for _ in range(N)]
+    for rnd, (active, arrived) in enumerate(rounds):
+        if rnd == 3:
+            note("saving every peer's error feedback to host and restoring it into new buffers")
+            saved = [e.cpu().numpy().copy() for e in ef_g]
+            del ef_g
+            torch.cuda.synchronize()
+            ef_g = [torch.from_numpy(s).cuda() for s in saved]
+        pay_o, sc_o = {}, {}
+        for p in active:
+            step = (datagen.lognormal(n, W, p + 11, 90 + rnd).numpy() * np.float32(1e-3)).astype(np.float32)
+            post_o = (theta_o - step).astype(np.float32)
+            pay_o[p], sc_o[p], ef_o[p] = orc.compress(orc.pseudo_gradient(theta_o, post_o), ef_o[p], beta=0.95)
+            note(f"participation round {rnd} peer {p}: sl_compress_weights")
+            sl.sl_compress_weights(theta_g, torch.from_numpy(post_o).cuda(), ef_g[p], 0.95, pay_g[p], sc_g[p])
+        got = [p for p in arrived]
+        sum_o = orc.aggregate([pay_o[p] for p in got], [sc_o[p] for p in got], n)
+        if not got:
+            out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+            note(f"participation round {rnd}: sl_aggregate over no peers")
+            sl.sl_aggregate([], [], out)
+            torch.cuda.synchronize()
+            assert_bitwise(out.cpu().numpy(), sum_o, f"round {rnd} empty sum")
+            assert not np.signbit(sum_o).any() and not sum_o.any()
+        elif rnd == 3:
+            rec = torch.stack([pay_g[p] for p in got], dim=1).contiguous()
+            sc = torch.stack([sc_g[p] for p in got], dim=1).contiguous()
+            note(f"participation round {rnd}: sl_aggregate_apply_interleaved, {len(got)} peer(s)")
+            sl.sl_aggregate_apply_interleaved(rec, sc, theta_g)
+            theta_o = orc.apply_mean(theta_o, sum_o, len(got))
+        elif rnd == 4:
+            rec = torch.stack([pay_g[p] for p in got], dim=1).contiguous()
+            sc = torch.stack([sc_g[p] for p in got], dim=1).contiguous()
+            out = torch.empty(n, dtype=torch.float32, device="cuda")
+            note(f"participation round {rnd}: sl_aggregate_interleaved + sl_apply_mean, {len(got)} peers")
+            sl.sl_aggregate_interleaved(rec, sc, out)
+            sl.sl_apply_mean(theta_g, out, len(got))
+            theta_o = orc.apply_mean(theta_o, sum_o, len(got))
+        else:
+            note(f"participation round {rnd}: sl_aggregate_apply over peers {got}")
+            sl.sl_aggregate_apply([pay_g[p] for p in got], [sc_g[p] for p in got], theta_g)
+            theta_o = orc.apply_mean(theta_o, sum_o, len(got))
+        torch.cuda.synchronize()
+        for p in active:
+            assert_bitwise(pay_g[p].cpu().numpy(), pay_o[p], f"round {rnd} peer {p} records")
+            assert_bitwise(sc_g[p].cpu().numpy(), sc_o[p], f"round {rnd} peer {p} scales")
+        for p in range(N):
+            assert_bitwise(ef_g[p].cpu().numpy(), ef_o[p], f"round {rnd} peer {p} ef")
+        assert_bitwise(theta_g.cpu().numpy(), theta_o, f"round {rnd} theta")
