@@ -252,11 +252,16 @@ def test_peerset_matches_lists_and_follows_buffer_contents(orc):
     assert not flags.cpu().numpy().any()
 
 
+# Every chunk is compared when the span has at most this many elements (every
+# case below; larger spans would be sampled).
+FULL_CHECK_ELEMS = 1 << 30
+
+
 # Records too large for the last-level cache (more than 224 MiB of records and
 # scales in one call) are summed three chunks per wavefront up to 54 peers and
 # two up to 81.  Peer counts at both ends of every variant of that kernel, and
 # beyond it; odd chunk counts, one or two past a multiple of three, leave the
-# last wavefront a partial run.
+# last wavefront a partial run.  Every chunk is compared.
 @pytest.mark.parametrize("n_peers", [9, 10, 18, 19, 27, 28, 54, 55, 81, 82, 128])
 def test_records_beyond_cache(orc, n_peers):
     sl = require_gpu()
@@ -267,7 +272,10 @@ def test_records_beyond_cache(orc, n_peers):
     base = orc.pack(idx, code)
     del idx, code
     rng = np.random.default_rng(n_peers)
-    sample = np.unique(np.r_[0, 1, 2, C - 3, C - 2, C - 1, rng.choice(C, 300, replace=False)])
+    if C * 4096 <= FULL_CHECK_ELEMS:
+        sample = np.arange(C)
+    else:
+        sample = np.unique(np.r_[0, 1, 2, C - 3, C - 2, C - 1, rng.choice(C, 300, replace=False)])
     pay_g, sc_g, pay_o, sc_o = [], [], [], []
     for p in range(n_peers):
         shift = (7919 * p) % C
@@ -320,8 +328,9 @@ def test_interleaved_records(orc, n_peers):
     assert_bitwise(got, orc.aggregate(payloads, scales, n), f"interleaved, {n_peers} peers")
 
 
-# Records larger than the last-level cache, every variant; sampled chunks
-# (the first, the last three, 300 random) bitwise and every output written.
+# Records larger than the last-level cache, every variant; every chunk bitwise
+# (up to FULL_CHECK_ELEMS elements, else the first, the last three and 300
+# random ones) and every output written.
 @pytest.mark.parametrize("n_peers", [24, 48, 64, 128])
 def test_interleaved_records_beyond_cache(orc, n_peers):
     sl = require_gpu()
@@ -331,7 +340,10 @@ def test_interleaved_records_beyond_cache(orc, n_peers):
     base = orc.pack(idx, code)
     del idx, code
     rng = np.random.default_rng(50 + n_peers)
-    sample = np.unique(np.r_[0, 1, 2, C - 3, C - 2, C - 1, rng.choice(C, 300, replace=False)])
+    if C * 4096 <= FULL_CHECK_ELEMS:
+        sample = np.arange(C)
+    else:
+        sample = np.unique(np.r_[0, 1, 2, C - 3, C - 2, C - 1, rng.choice(C, 300, replace=False)])
     rec = np.empty((C, n_peers, 112), np.uint8)
     sc = np.empty((C, n_peers), np.float32)
     pay_o, sc_o = [], []
