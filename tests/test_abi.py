@@ -369,3 +369,17 @@ def test_header_compiles_as_c99_and_links(lib, tmp_path):
                     f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.split() == ["OK", "112"], (out.stdout, out.stderr)
+
+
+def test_c_roundtrip_program_compiles(lib, tmp_path):
+    """The C host program of the C-boundary GPU test (tests/c/sl_c_roundtrip.c)
+    builds as C99 with warnings as errors against the header, the library and
+    the HIP runtime; run without arguments it prints its usage and exits 1
+    before touching the GPU."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("sl_c_build", os.path.join(ROOT, "tests", "c", "build.py"))
+    c_build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(c_build)
+    exe = c_build.build_c_roundtrip(out=str(tmp_path / "sl_c_roundtrip"))
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr, (r.returncode, r.stderr)
