@@ -29,7 +29,9 @@
 //
 // Records are 112 bytes, so neighbouring chunks share 128-byte lines.  Work-
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
-// each XCD a contiguous range so a shared line is read through one L2.
+// each XCD a contiguous range so a shared line is read through one L2.  The
+// kernels for records laid out chunk-major across peers (one contiguous span
+// per chunk) take the chunks in linear order instead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
