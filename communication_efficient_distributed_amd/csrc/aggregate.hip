@@ -334,7 +334,13 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
 // Every chunk's records are loaded up front, so the later chunks' arrive while
 // the first is summed; they are awaited before the first chunk's stores are
 // issued, so that no wait on a load covers any store.  Each chunk goes through
-// the same operations, in the same order, as in aggregate_kernel.
+// the same operations, in the same order, as in aggregate_kernel.  In a full
+// run a lane fetches its peer's CPW adjacent scales with one 8- or 12-byte
+// load instead of one load per chunk: that cut the kernel's time by 6-8% at
+// 36-64 peers and 1.7% at the decoder block (8192 x 28672 with records from
+// HBM: 248 / 276 / 288 / 310 us at 36 / 48 / 54 / 64 peers against 234 / 254 /
+// 264 / 289 us; decoder block, 24 peers, 765 against 752 us), since every
+// scale load of nine peers is nine separate cache-line requests.
 template <int NGMAX, int CPW>
 __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, int32_t n_peers, float* out,
                                                               int64_t n_chunks, int64_t per_xcd) {
@@ -347,8 +353,40 @@ __global__ __launch_bounds__(kWave) void aggregate_run_kernel(PeerTable peers, i
     ChunkRecords<NGMAX> cr[CPW];
     LanePeers<NGMAX> lp;
     lane_peers<NGMAX>(peers, n_peers, lane, lp);
+    if (count == CPW) {
+        // A full run: every chunk's records, then each peer's CPW scales,
+        // which are adjacent, in one load per group of nine peers.
+        typedef const __attribute__((address_space(1))) float gfloat;
+        typedef float f3 __attribute__((ext_vector_type(3), aligned(4)));
+        typedef float f2 __attribute__((ext_vector_type(2), aligned(4)));
+        typedef const __attribute__((address_space(1))) f3 gf3;
+        typedef const __attribute__((address_space(1))) f2 gf2;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) load_records_at<NGMAX>(lp, i < count ? c0 + i : c0, cr[i]);
+        for (int i = 0; i < CPW; ++i) {
+#pragma unroll
+            for (int g = 0; g < NGMAX; ++g)
+                cr[i].r[g] = load_record16(lp.rec[g] + (size_t)(c0 + i) * SL_PAYLOAD_BYTES);
+        }
+#pragma unroll
+        for (int g = 0; g < NGMAX; ++g) {
+            if constexpr (CPW == 3) {
+                const f3 v = *(gf3*)(lp.sc[g] + c0);
+                cr[0].sv[g] = v.x;
+                cr[1].sv[g] = v.y;
+                cr[2].sv[g] = v.z;
+            } else if constexpr (CPW == 2) {
+                const f2 v = *(gf2*)(lp.sc[g] + c0);
+                cr[0].sv[g] = v.x;
+                cr[1].sv[g] = v.y;
+            } else {
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) cr[i].sv[g] = *(gfloat*)(lp.sc[g] + c0 + i);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) load_records_at<NGMAX>(lp, i < count ? c0 + i : c0, cr[i]);
+    }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         if (i < count) {
