@@ -643,8 +643,10 @@ MANY_PEERS = (36, 48, 55, 64, 81, 128)
 
 def many_peers(sl, dev, reps):
     """The aggregate at 8192 x 28672 with more peers than the step's 24: 36 to
-    128 distinct peers' records (240 to 850 MB, beyond the last-level cache,
-    so every call reads them from HBM), each count timed back to back."""
+    128 distinct peers' records (240 to 850 MB per set), each count timed back
+    to back over two independent record sets taken in turn, so that every call
+    reads its records from HBM (one set re-read would stay partly in the
+    256 MB last-level cache)."""
     import torch
 
     from communication_efficient_distributed_amd import datagen
@@ -654,8 +656,9 @@ def many_peers(sl, dev, reps):
     C = n // CHUNK
     stream = torch.cuda.current_stream(dev)
     ef = torch.empty(n, dtype=torch.float32, device=dev)
+    M = max(MANY_PEERS)
     pp, ps = [], []
-    for p in range(1, max(MANY_PEERS) + 1):
+    for p in range(1, 2 * M + 1):   # set 0: peers 1..M, set 1: peers M+1..2M
         d = datagen.student_t3(n, W, p, 0, dev)
         ef.zero_()
         x, y = sl.compress(d, ef, BETA)
@@ -664,15 +667,15 @@ def many_peers(sl, dev, reps):
         del d
     del ef
     out = torch.empty(n, dtype=torch.float32, device=dev)
-    res = {"params": n, "chunks": C}
+    res = {"params": n, "chunks": C, "record_sets": 2}
     for P in MANY_PEERS:
-        peers = sl.PeerSet(pp[:P], ps[:P])
-        for _ in range(3):
-            sl.sl_aggregate(peers, None, out)
+        sets = [sl.PeerSet(pp[:P], ps[:P]), sl.PeerSet(pp[M:M + P], ps[M:M + P])]
+        for k in range(3):
+            sl.sl_aggregate(sets[k % 2], None, out)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
-            sl.sl_aggregate(peers, None, out)
+        for k in range(reps):
+            sl.sl_aggregate(sets[k % 2], None, out)
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / reps
@@ -683,20 +686,20 @@ def many_peers(sl, dev, reps):
     # The same records laid out chunk-major across peers (sl_aggregate_interleaved).
     il = {}
     for P in MANY_PEERS:
-        r_, s_ = interleaved_records(torch, pp[:P], ps[:P])
-        for _ in range(3):
-            sl.sl_aggregate_interleaved(r_, s_, out)
+        ils = [interleaved_records(torch, pp[:P], ps[:P]), interleaved_records(torch, pp[M:M + P], ps[M:M + P])]
+        for k in range(3):
+            sl.sl_aggregate_interleaved(*ils[k % 2], out)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
-            sl.sl_aggregate_interleaved(r_, s_, out)
+        for k in range(reps):
+            sl.sl_aggregate_interleaved(*ils[k % 2], out)
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / reps
         bpp = 4 + P * RECORD / CHUNK
         gbs = bpp * n / (t * 1e-3) / 1e9
         il[str(P)] = {"ms": round(t, 5), "gb_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-        del r_, s_
+        del ils
     res["interleaved"] = il
     del pp, ps, out
     torch.cuda.synchronize()
