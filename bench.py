@@ -667,7 +667,8 @@ def many_peers(sl, dev, reps):
         del d
     del ef
     out = torch.empty(n, dtype=torch.float32, device=dev)
-    res = {"params": n, "chunks": C, "record_sets": 2}
+    res = {"params": n, "chunks": C, "record_sets": 2,
+           "note": "per count, two independent record sets taken in turn: every call reads its records from HBM"}
     for P in MANY_PEERS:
         sets = [sl.PeerSet(pp[:P], ps[:P]), sl.PeerSet(pp[M:M + P], ps[M:M + P])]
         for k in range(3):
