@@ -811,8 +811,9 @@ hipError_t launch_apply_mean(float* theta, const float* out, int32_t n_peers, in
                              hipStream_t stream) {
     const int64_t n_chunks = n / SL_CHUNK;
     float nf = (float)n_peers;
-    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
-        int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+    const int64_t per = stream_launch_chunks(n_chunks);
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
+        int64_t m = n_chunks - c0 < per ? n_chunks - c0 : per;
         float* st = theta + (size_t)c0 * SL_CHUNK;
         const float* so = out + (size_t)c0 * SL_CHUNK;
         void* args[] = {(void*)&st, (void*)&so, (void*)&nf, (void*)&m};

@@ -504,12 +504,14 @@ constexpr int kCapWeights = 5;
 static_assert(cap_is_exact(kCapCompress, sizeof(Shared)) && cap_is_exact(kCapWeights, sizeof(Shared)),
               "residency caps");
 
-// One launch per kLaunchChunks chunks, each on its own slice of every buffer.
+// Equal launches of at most kStreamLaunchChunks chunks, each on its own slice
+// of every buffer.
 template <bool WEIGHTS>
 hipError_t launch_segments(const float* a, const float* b, float* ef, float beta, uint8_t* payload, float* scales,
                            int64_t n_chunks, int cap, hipStream_t stream) {
-    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
-        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+    const int64_t per = stream_launch_chunks(n_chunks);
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
+        const int64_t m = n_chunks - c0 < per ? n_chunks - c0 : per;
         const size_t e0 = (size_t)c0 * SL_CHUNK;
         const float* sa = a + e0;
         const float* sb = WEIGHTS ? b + e0 : b;

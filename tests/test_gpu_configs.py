@@ -172,6 +172,8 @@ def test_flat_16b_span_sampled(orc):
     dev = torch.device("cuda:0")
     special = [0, C - 1, (1 << 31) // CHUNK - 1, (1 << 31) // CHUNK, (1 << 32) // CHUNK - 1,
                (1 << 32) // CHUNK, (1 << 32) // (4 * CHUNK), (1 << 32) // (4 * CHUNK) - 1]
+    per = -(-C // -(-C // (1 << 16)))    # chunks per streaming launch (60 launches)
+    special += [per - 1, per, 59 * per - 1, 59 * per]
     idx = sample_chunks(C, special, 4096, seed=5)
     m = idx.size
 
@@ -220,12 +222,15 @@ def test_flat_16b_span_sampled(orc):
 
 
 def test_span_split_over_launches_sampled(orc):
-    """A span of 2^22 + 3 chunks (17.2e9 parameters), one chunk past where the
-    library splits a call into several kernel launches: compress (two rounds),
-    compress from weights, 2-peer aggregate, fused aggregate-apply and
-    apply_mean, then the aggregate and the fused update on the same records laid
-    out chunk-major, compared with the oracle on sampled chunks that include
-    both sides of the split."""
+    """A span of 2^22 + 3 chunks (17.2e9 parameters), past where the library
+    splits an aggregate call into two kernel launches (2^22 chunks each at
+    most; the streaming kernels, compress and apply_mean, split long calls
+    into equal launches of at most 2^16 chunks, here 65 of 64,528): compress
+    (two rounds), compress from weights, 2-peer aggregate, fused
+    aggregate-apply and apply_mean, then the aggregate and the fused update on
+    the same records laid out chunk-major, compared with the oracle on sampled
+    chunks that include both sides of the 2^22 split and of the first and last
+    streaming-launch boundaries."""
     sl = require_gpu()
     W = datagen.FLAT_16B
     K = 1 << 22
@@ -236,7 +241,10 @@ def test_span_split_over_launches_sampled(orc):
         pytest.skip(f"needs {need / 2**30:.0f} GiB of free device memory")
     T = oracle_threads()
     dev = torch.device("cuda:0")
-    idx = sample_chunks(C, [0, 1, K - 2, K - 1, K, K + 1, K + 2], 512, seed=7)
+    parts = -(-C // (1 << 16))
+    per = -(-C // parts)                 # chunks per streaming launch
+    last = (parts - 1) * per
+    idx = sample_chunks(C, [0, 1, per - 1, per, last - 1, last, K - 2, K - 1, K, K + 1, K + 2], 512, seed=7)
     m = idx.size
 
     a = torch.empty(n, dtype=torch.float32, device=dev)
