@@ -795,10 +795,14 @@ hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* sca
     return hipSuccess;
 }
 
+// Split like the streaming kernels: at the decoder block, 24 and 36 peers,
+// four launches measured 0.785-0.787 and 0.760-0.763 of HBM against
+// 0.756-0.759 and 0.736-0.742 in one (records from HBM).
 hipError_t launch_aggregate_apply_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
                                               float* theta, int64_t n_chunks, hipStream_t stream) {
-    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
-        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+    const int64_t per = stream_launch_chunks(n_chunks);
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
+        const int64_t m = n_chunks - c0 < per ? n_chunks - c0 : per;
         const hipError_t e = launch_apply_interleaved_one(records + (size_t)c0 * (size_t)n_peers * SL_PAYLOAD_BYTES,
                                                           scales + (size_t)c0 * (size_t)n_peers, n_peers,
                                                           theta + (size_t)c0 * SL_CHUNK, m, stream);
