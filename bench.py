@@ -946,6 +946,29 @@ MLP_PARAMS = 8192 * 28672
 DECODER_PARAMS = 855_638_016
 WORKLOAD_CHUNKS = {256: "1M", 16384: "8192x8192", 57344: "8192x28672", 208896: "decoder block",
                    3906250: "16e9 span"}
+# The streaming kernels (compress, compress from weights, apply_mean, the fused
+# update on chunk-major records) run a long call as equal launches of at most
+# 2^16 chunks (stream_launch_chunks in csrc/internal.h); their trace rows are
+# labelled with the workload the launches belong to.
+STREAM_LAUNCH_CHUNKS = 1 << 16
+
+
+def _split_launch_labels():
+    labels = {}
+    for c, name in WORKLOAD_CHUNKS.items():
+        parts = -(-c // STREAM_LAUNCH_CHUNKS)
+        if parts <= 1:
+            continue
+        per = -(-c // parts)
+        last = c - (parts - 1) * per
+        labels[per] = f"{name}, {parts} launches of {per} chunks" if last == per else \
+            f"{name}, {parts - 1} of {parts} launches ({per} chunks)"
+        if last != per:
+            labels[last] = f"{name}, last of {parts} launches ({last} chunks)"
+    return labels
+
+
+SPLIT_LAUNCH_LABELS = _split_launch_labels()
 
 
 def _csv_rows(path):
@@ -1268,7 +1291,8 @@ def summarize_trace(base, outdir):
         else:
             chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
             lab = role.get(id(d), "").replace("_timed", "")
-            label = f"{name} [{WORKLOAD_CHUNKS.get(chunks, f'{chunks} chunks')}{suffix.get(lab, '')}]"
+            where = WORKLOAD_CHUNKS.get(chunks) or SPLIT_LAUNCH_LABELS.get(chunks, f"{chunks} chunks")
+            label = f"{name} [{where}{suffix.get(lab, '')}]"
             if d["peers"] > 1:
                 label += f" x{d['peers']} peers"
         lab = role.get(id(d))
