@@ -783,10 +783,14 @@ hipError_t launch_apply_interleaved_one(const uint8_t* records, const float* sca
     return hipLaunchKernel(k, grid, dim3(kWave), args, 0, stream);
 }
 
+// Split like the streaming kernels (the chunks are taken in linear order):
+// the 16e9-parameter span, 24 peers, ran 12.76 ms = 0.733 of HBM in 60
+// launches against 13.22 ms = 0.708 in one.
 hipError_t launch_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, float* out,
                                         int64_t n_chunks, hipStream_t stream) {
-    for (int64_t c0 = 0; c0 < n_chunks; c0 += kLaunchChunks) {
-        const int64_t m = n_chunks - c0 < kLaunchChunks ? n_chunks - c0 : kLaunchChunks;
+    const int64_t per = stream_launch_chunks(n_chunks);
+    for (int64_t c0 = 0; c0 < n_chunks; c0 += per) {
+        const int64_t m = n_chunks - c0 < per ? n_chunks - c0 : per;
         const hipError_t e = launch_interleaved_one(records + (size_t)c0 * (size_t)n_peers * SL_PAYLOAD_BYTES,
                                                     scales + (size_t)c0 * (size_t)n_peers, n_peers,
                                                     out + (size_t)c0 * SL_CHUNK, m, stream);

@@ -16,19 +16,23 @@ namespace sl {
 // changes no result.
 constexpr int64_t kLaunchChunks = int64_t(1) << 22;
 
-// The streaming kernels (compress, compress from weights, apply_mean, and the
-// fused update on chunk-major records) split a long call further, into equal
+// The streaming kernels (compress, compress from weights, apply_mean) and the
+// chunk-major aggregate and fused update split a long call further, into equal
 // launches of at most kStreamLaunchChunks chunks: one launch per call up to
 // 8192 x 28672 parameters, four for a decoder block, 60 for the
-// 16e9-parameter span.  Measured on lognormal
-// values: the decoder block's compress, compress from weights and apply_mean
+// 16e9-parameter span.  Measured on lognormal values: the decoder block's
+// compress, compress from weights and apply_mean
 // ran at 0.777-0.784, 0.780-0.785 and 0.791-0.793 of HBM in one launch against
 // 0.799-0.802, 0.799-0.802 and 0.818-0.826 in three to five; the 16e9 span at
 // 0.742-0.752, 0.748-0.751 and 0.761 against 0.763-0.767, 0.761-0.764 and
 // 0.786-0.790 in 48 to 80.  Much smaller launches lose to their tails (8192 x
-// 28672 in four launches: 0.775 against 0.792).  The aggregate kernels keep
-// one launch: splitting measured slower for the per-peer ones and no faster
-// for the chunk-major one.
+// 28672 in four launches: 0.775 against 0.792).  These kernels take their
+// chunks in linear order and the dispatcher deals workgroups to the XCDs
+// round-robin; the loss in long launches fits the eight XCDs' fronts drifting
+// apart, which a launch boundary undoes (giving each XCD its own range of
+// chunks outright measured 4-6% slower still).  The per-peer aggregate kernels
+// use such ranges on purpose and keep one launch: splitting them measured
+// slower.
 constexpr int64_t kStreamLaunchChunks = int64_t(1) << 16;
 
 // Chunks per launch for a streaming kernel over n_chunks chunks.
