@@ -454,3 +454,39 @@ def test_interleaved_overlapping_indices_and_extreme_scales(orc):
     sl.sl_aggregate_apply_interleaved(torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda(), theta)
     torch.cuda.synchronize()
     assert_bitwise(theta.cpu().numpy(), orc.apply_mean(theta0, want, 3), "fused interleaved over all binades")
+
+
+# 65,537 chunks: one more than the longest single launch of the chunk-major
+# kernels, so each call runs as two launches (32,769 and 32,768 chunks); every
+# output compared, for the aggregate and the fused update.
+@pytest.mark.parametrize("n_peers", [24, 36])
+def test_interleaved_split_launches(orc, n_peers):
+    sl = require_gpu()
+    C = (1 << 16) + 1
+    n = C * 4096
+    idx, code, s0 = datagen.random_entries_bulk(C, seed=6000 + n_peers)
+    base = orc.pack(idx, code)
+    del idx, code
+    rec = np.empty((C, n_peers, 112), np.uint8)
+    sc = np.empty((C, n_peers), np.float32)
+    pay_o, sc_o = [], []
+    for p in range(n_peers):
+        shift = (7919 * p + 29) % C
+        rec[:, p, :] = np.roll(base, shift, axis=0)
+        sc[:, p] = np.roll(s0, shift) * np.float32(1.0 + p / 8.0)
+        pay_o.append(np.ascontiguousarray(rec[:, p, :]))
+        sc_o.append(np.ascontiguousarray(sc[:, p]))
+    rec_g, sc_g = torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda()
+    del rec, sc
+    want = orc.aggregate(pay_o, sc_o, n, nthreads=oracle_threads())
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    note(f"sl_aggregate_interleaved over two launches: n_peers={n_peers} chunks={C}")
+    sl.sl_aggregate_interleaved(rec_g, sc_g, out)
+    torch.cuda.synchronize()
+    assert_bitwise(out.cpu().numpy(), want, f"interleaved over two launches, {n_peers} peers")
+    theta0 = datagen.theta0(n, datagen.SMALL_1M).numpy()
+    theta = torch.from_numpy(theta0.copy()).cuda()
+    note(f"sl_aggregate_apply_interleaved over two launches: n_peers={n_peers} chunks={C}")
+    sl.sl_aggregate_apply_interleaved(rec_g, sc_g, theta)
+    torch.cuda.synchronize()
+    assert_bitwise(theta.cpu().numpy(), orc.apply_mean(theta0, want, n_peers), f"fused over two launches, {n_peers} peers")
