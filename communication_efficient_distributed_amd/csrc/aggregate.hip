@@ -31,7 +31,8 @@
 // groups are dispatched to the 8 XCDs round-robin; the chunk numbering gives
 // each XCD a contiguous range so a shared line is read through one L2.  The
 // kernels for records laid out chunk-major across peers (one contiguous span
-// per chunk) take the chunks in linear order instead.
+// per chunk) and the fused update up to 81 peers, whose theta stream
+// dominates, take the chunks in linear order instead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -310,7 +311,12 @@ __global__ __launch_bounds__(kWave) void aggregate_kernel(PeerTable peers, int32
     __shared__ __align__(16) float tile[SL_CHUNK];
     __shared__ __align__(16) uint32_t stage[(kPeersPerLoad + 1) * kRecWords];
     const int lane = (int)threadIdx.x;
-    const int64_t chunk = xcd_chunk(per_xcd);
+    // The fused update takes its chunks in linear order up to 81 peers (8192 x
+    // 28672, records from HBM: 36 / 64 peers 0.725-0.727 / 0.671-0.678 of HBM
+    // against 0.705-0.708 / 0.662-0.664 with XCD ranges); at 128 peers the
+    // records' shared lines weigh more and the XCD ranges won (0.556-0.561
+    // against 0.544-0.547).
+    const int64_t chunk = (APPLY && NGMAX <= 9) ? (int64_t)blockIdx.x : xcd_chunk(per_xcd);
     if (chunk >= n_chunks) return;
     float* dst_chunk = dst + (size_t)chunk * SL_CHUNK;
     if (!APPLY && n_peers == 0) {  // the empty sum; the peer table is empty
@@ -511,7 +517,12 @@ __global__ __launch_bounds__(kWave * kApplyWaves) void aggregate_apply4_kernel(P
     const int tid = (int)threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t chunk = xcd_chunk(per_xcd);
+    // Linear chunk order: theta's read and write are 8 of the 8.68 bytes per
+    // parameter at 24 peers, and the device streams them best as one front
+    // (decoder block, 24 peers, records from HBM: 0.767 of HBM against 0.731
+    // with each XCD on its own range; 8192 x 28672 cached 0.803 against 0.798).
+    const int64_t chunk = (int64_t)blockIdx.x;
+    (void)per_xcd;
     if (chunk >= n_chunks) return;  // the whole workgroup
     float* th_chunk = theta + (size_t)chunk * SL_CHUNK;
     v4f th[kQuarterSlots];
