@@ -191,7 +191,10 @@ sl_status sl_apply_mean(float* theta, const float* out, int32_t n_peers, int64_t
  * out      out float32[n], 16-byte aligned, fully overwritten; must not overlap
  *          records or scales
  * n        number of parameters, a multiple of SL_CHUNK
- * Payloads are trusted, as for sl_aggregate.
+ * Payloads are trusted, as for sl_aggregate.  Records in this layout are
+ * validated by sl_validate_payload over the buffers viewed as
+ * n / 4096 * n_peers records: each record is checked on its own, so the flags
+ * come back in the same chunk-major order.
  */
 sl_status sl_aggregate_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
                                    float* out, int64_t n, void* stream);

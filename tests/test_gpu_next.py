@@ -389,3 +389,25 @@ def test_rounds_with_changing_participation_and_ef_resume(orc):
         for p in range(N):
             assert_bitwise(ef_g[p].cpu().numpy(), ef_o[p], f"round {rnd} peer {p} ef")
         assert_bitwise(theta_g.cpu().numpy(), theta_o, f"round {rnd} theta")
+
+
+def test_validate_chunk_major_records(orc):
+    """Records laid out chunk-major across peers (the layout of
+    sl_aggregate_interleaved) are validated by sl_validate_payload over the
+    buffer viewed as C * N records: every record is checked on its own, so the
+    flags come back chunk-major, flag [c, p] for peer p's record of chunk c.
+    24 peers of a ragged 1000 records with planted defects, against the
+    oracle's per-peer flags."""
+    sl = require_gpu()
+    N, C = 24, 1000
+    payloads, scales = defective_peers(orc, N, C, 77)
+    rec = np.ascontiguousarray(np.stack(payloads, axis=1))       # [C, N, 112]
+    sc = np.ascontiguousarray(np.stack(scales, axis=1))          # [C, N]
+    want = np.stack([orc.validate(payloads[p], scales[p])[1] for p in range(N)], axis=1)
+    assert (want != 0).sum() > 0
+    flags = torch.full((C * N,), 255, dtype=torch.uint8, device="cuda")
+    note("sl_validate_payload over chunk-major records, 24 peers x 1000")
+    sl.sl_validate_payload(torch.from_numpy(rec.reshape(C * N, 112)).cuda(),
+                           torch.from_numpy(sc.reshape(C * N)).cuda(), flags)
+    torch.cuda.synchronize()
+    assert_bitwise(flags.cpu().numpy().reshape(C, N), want, "chunk-major flags")
