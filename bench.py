@@ -469,6 +469,12 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     stats = lambda: sl.sl_peer_stats(peers, None, counts, smax, flags=flags_all)
     t = timed(stats)
     res["peer_stats_24_peers"] = add_back_to_back(kstats(t, bpp, timed.samples), stats, bpp)
+    # the same statistics on the records laid out chunk-major across peers
+    il_r, il_s = interleaved_records(torch, peer_p, peer_s)
+    stats_il = lambda: sl.sl_peer_stats_interleaved(il_r, il_s, counts, smax, flags=flags_all)
+    t = timed(stats_il)
+    res["peer_stats_24_peers_chunk_major"] = add_back_to_back(kstats(t, bpp, timed.samples), stats_il, bpp)
+    del il_r, il_s
     res["small_round_1m"] = small_round(sl, delta.device)
     return res
 

@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     sl_compress_host_ef,
     sl_compress_weights,
     sl_peer_stats,
+    sl_peer_stats_interleaved,
     sl_status_string,
     sl_validate_payload,
     sl_validate_payloads,

@@ -31,7 +31,7 @@ STATUS = {
 EXPORTS = ("sl_compress", "sl_compress_weights", "sl_aggregate", "sl_aggregate_interleaved", "sl_aggregate_apply",
            "sl_aggregate_apply_interleaved",
            "sl_apply_mean", "sl_validate_payload", "sl_validate_payloads", "sl_peer_stats",
-           "sl_peer_stats_noalloc", "sl_host_device_pointer", "sl_status_string")
+           "sl_peer_stats_interleaved", "sl_peer_stats_noalloc", "sl_host_device_pointer", "sl_status_string")
 
 
 class SparseLoCoError(RuntimeError):
@@ -68,6 +68,8 @@ def load():
     L.sl_validate_payloads.restype = ctypes.c_int
     L.sl_peer_stats.argtypes = [P, P, I32, I64, P, P, P, P]
     L.sl_peer_stats.restype = ctypes.c_int
+    L.sl_peer_stats_interleaved.argtypes = [P, P, I32, I64, P, P, P, P]
+    L.sl_peer_stats_interleaved.restype = ctypes.c_int
     L.sl_peer_stats_noalloc.argtypes = [P, P, I32, I64, P, P, P, P]
     L.sl_peer_stats_noalloc.restype = ctypes.c_int
     L.sl_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
@@ -240,6 +242,35 @@ def sl_peer_stats(payloads, scales, counts: torch.Tensor, scale_max: torch.Tenso
     with torch.cuda.device(counts.device):
         _check(name, getattr(load(), name)(pa, sa, ctypes.c_int32(N), ctypes.c_int64(n_chunks), f, c, m,
                                            _stream_of(counts, stream)))
+
+
+def sl_peer_stats_interleaved(records: torch.Tensor, scales: torch.Tensor, counts: torch.Tensor,
+                              scale_max: torch.Tensor, flags=None, stream=None) -> None:
+    """sl_peer_stats on records laid out chunk-major across peers (records
+    uint8 [n_chunks, n_peers, 112], scales float32 [n_chunks, n_peers]);
+    counts, scale_max and flags ([n_peers, n_chunks]) per peer, as
+    sl_peer_stats writes them."""
+    if records.dim() != 3 or records.shape[2] != SL_PAYLOAD_BYTES:
+        raise ValueError("records must be a [n_chunks, n_peers, 112] tensor")
+    C, N = records.shape[0], records.shape[1]
+    if scales.dim() != 2 or tuple(scales.shape) != (C, N):
+        raise ValueError("scales must be a [n_chunks, n_peers] tensor")
+    if counts.dim() != 2 or tuple(counts.shape) != (N, 4):
+        raise ValueError("counts must be a [n_peers, 4] tensor")
+    if scale_max.numel() != N:
+        raise ValueError("scale_max must hold n_peers floats")
+    if flags is not None and (flags.dim() != 2 or tuple(flags.shape) != (N, C)):
+        raise ValueError("flags must be a [n_peers, n_chunks] tensor")
+    if N and C:
+        r, s = _dev(records, "records", torch.uint8), _dev(scales, "scales", torch.float32)
+    else:
+        r = s = ctypes.c_void_p(None)
+    c = _dev(counts, "counts", torch.int64)
+    m = _dev(scale_max, "scale_max", torch.float32)
+    f = _dev(flags, "flags", torch.uint8) if flags is not None else ctypes.c_void_p(None)
+    with torch.cuda.device(counts.device):
+        _check("sl_peer_stats_interleaved", load().sl_peer_stats_interleaved(r, s, ctypes.c_int32(N), ctypes.c_int64(C),
+                                                                             f, c, m, _stream_of(counts, stream)))
 
 
 class PeerSet:

@@ -81,7 +81,8 @@ size_t peer_stats_scratch_bytes();
 // (peer_stats_scratch_bytes() bytes; the counters are zero at load).
 hipError_t peer_stats_static_scratch(void** ptr);
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
-                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream);
+                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream,
+                             int64_t rec_stride = SL_PAYLOAD_BYTES, int64_t sc_stride = 1);
 
 hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
                                    float beta, uint8_t* payload, float* scales, int64_t n_chunks,

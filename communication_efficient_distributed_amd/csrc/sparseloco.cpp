@@ -202,6 +202,45 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
                                           static_cast<hipStream_t>(stream)));
 }
 
+sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales, int32_t n_peers, int64_t n_chunks,
+                                   uint8_t* flags, int64_t* counts, float* scale_max, void* stream) {
+    if (n_chunks < 0 || n_chunks > 0x7fffffff) return SL_ERR_SHAPE;
+    if (n_peers < 0 || n_peers > SL_MAX_PEERS) return SL_ERR_TOO_MANY_PEERS;
+    if (n_peers == 0) return SL_OK;
+    if (!counts || !scale_max) return SL_ERR_INVALID_ARG;
+    if (!aligned(counts, 8) || !aligned(scale_max, 4)) return SL_ERR_ALIGN;
+    const size_t cbytes = (size_t)n_peers * 4 * sizeof(int64_t);
+    const size_t mbytes = (size_t)n_peers * sizeof(float);
+    const size_t fbytes = flags ? (size_t)n_peers * (size_t)n_chunks : 0;
+    if (overlap(counts, cbytes, scale_max, mbytes) || overlap(flags, fbytes, counts, cbytes) ||
+        overlap(flags, fbytes, scale_max, mbytes))
+        return SL_ERR_INVALID_ARG;
+    sl::PeerTable table = {};
+    if (n_chunks > 0) {
+        if (!records || !scales) return SL_ERR_INVALID_ARG;
+        if (!aligned(records, 16) || !aligned(scales, 4)) return SL_ERR_ALIGN;
+        const size_t rbytes = (size_t)n_chunks * (size_t)n_peers * SL_PAYLOAD_BYTES;
+        const size_t sbytes = (size_t)n_chunks * (size_t)n_peers * sizeof(float);
+        const void* bufs[3] = {flags, counts, scale_max};
+        const size_t lens[3] = {fbytes, cbytes, mbytes};
+        for (int b = 0; b < 3; ++b)
+            if (overlap(bufs[b], lens[b], records, rbytes) || overlap(bufs[b], lens[b], scales, sbytes))
+                return SL_ERR_INVALID_ARG;
+        // Peer p's records start at its slot of chunk 0 and repeat every
+        // n_peers slots (the kernel's record and scale strides).
+        for (int32_t p = 0; p < n_peers; ++p) {
+            table.payload[p] = records + (size_t)p * SL_PAYLOAD_BYTES;
+            table.scales[p] = scales + p;
+        }
+    }
+    void* scratch = nullptr;
+    const sl_status ss = stats_scratch(stream, &scratch);
+    if (ss != SL_OK) return ss;
+    return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max, scratch,
+                                          static_cast<hipStream_t>(stream),
+                                          (int64_t)n_peers * SL_PAYLOAD_BYTES, (int64_t)n_peers));
+}
+
 sl_status sl_peer_stats_noalloc(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
                                 int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
                                 void* stream) {

@@ -127,7 +127,10 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 }
 
 // Grid (G, n_peers).  Workgroup g of peer p takes records g*256 + t +
-// k*G*256; flags (if given) as validate_kernel writes them.  Each workgroup
+// k*G*256; flags (if given) as validate_kernel writes them.  Peer p's record c
+// is at payload[p] + c * rec_stride and its scale at scales[p][c * sc_stride]:
+// strides 112 and 1 for per-peer buffers, n_peers * 112 and n_peers for
+// records laid out chunk-major across peers (payload[p] = records + 112 p).  Each workgroup
 // stores its five partial results in its own slot of the scratch, then counts
 // itself in the peer's arrival counter; the workgroup that arrives last (the
 // G-th) adds up the peer's G slots, writes the totals over
@@ -136,7 +139,8 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 // the arrival order.
 __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, int64_t n_chunks, uint8_t* flags,
                                                              uint64_t* counts, uint32_t* scale_max,
-                                                             uint64_t* slots, uint32_t* arrived) {
+                                                             uint64_t* slots, uint32_t* arrived,
+                                                             int64_t rec_stride, int64_t sc_stride) {
     __shared__ uint64_t part[kStatWaves][kStatValues];
     __shared__ uint32_t last;
     const int p = (int)blockIdx.y;
@@ -146,11 +150,11 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, in
     uint32_t bad = 0, zero = 0, mag = 0, neg = 0, mx = 0;
 #pragma unroll 2
     for (int64_t c = (int64_t)blockIdx.x * kStatThreads + tid; c < n_chunks; c += stride) {
-        const uint8_t* rec = peers.payload[p] + (size_t)c * SL_PAYLOAD_BYTES;
+        const uint8_t* rec = peers.payload[p] + (size_t)c * (size_t)rec_stride;
         uint32_t w[kIndexWords];
         load_indices(rec, w);
         const v4u cw = load_global16(rec + SL_INDEX_BYTES);
-        const float s = peers.scales[p][c];
+        const float s = peers.scales[p][(size_t)c * (size_t)sc_stride];
         const uint32_t f = record_flags(w, s);
         if (flags) flags[(size_t)p * (size_t)n_chunks + (size_t)c] = (uint8_t)f;
         bad += f ? 1u : 0u;
@@ -268,7 +272,8 @@ hipError_t peer_stats_static_scratch(void** ptr) {
 
 
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
-                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream) {
+                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream,
+                             int64_t rec_stride, int64_t sc_stride) {
     const int64_t per_peer = (kStatGroups + n_peers - 1) / n_peers;
     const int64_t needed = (n_chunks + kStatThreads - 1) / kStatThreads;
     const int64_t gx = needed < 1 ? 1 : needed < per_peer ? needed : per_peer;
@@ -280,8 +285,8 @@ hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_
     uint64_t* slots = reinterpret_cast<uint64_t*>(scratch_ptr);
     uint32_t* arrived = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(scratch_ptr) + kStatSlotBytes);
     PeerTable t = peers;
-    void* args[] = {(void*)&t, (void*)&n_chunks, (void*)&flags, (void*)&cnt, (void*)&mx, (void*)&slots,
-                    (void*)&arrived};
+    void* args[] = {(void*)&t,      (void*)&n_chunks, (void*)&flags,      (void*)&cnt,      (void*)&mx,
+                    (void*)&slots,  (void*)&arrived,  (void*)&rec_stride, (void*)&sc_stride};
     return hipLaunchKernel(reinterpret_cast<const void*>(&stats_kernel), dim3((unsigned)gx, (unsigned)n_peers),
                            dim3(kStatThreads), args, 0, stream);
 }

@@ -295,6 +295,31 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
                         void* stream);
 
 /*
+ * sl_peer_stats_interleaved -- sl_peer_stats for records laid out chunk-major
+ * across peers (the layout of sl_aggregate_interleaved).
+ *
+ * The same statistics ([SF] "What the Blockchain Does (and Doesn't Do)"; same
+ * reading) and the same flags as sl_peer_stats, for records where chunk
+ * c's record from peer p is at records + (c * n_peers + p) * 112 and its scale
+ * at scales[c * n_peers + p].  flags, counts and scale_max are laid out per
+ * peer, exactly as sl_peer_stats writes them.
+ *
+ * records    in  DEVICE uint8[n_chunks][n_peers][112], 16-byte aligned
+ * scales     in  DEVICE float32[n_chunks][n_peers], 4-byte aligned
+ * n_peers        0..SL_MAX_PEERS (0 does nothing)
+ * n_chunks       records per peer, 0..2^31-1
+ * flags      out DEVICE uint8[n_peers][n_chunks] or NULL
+ * counts     out DEVICE int64[n_peers][4], 8-byte aligned
+ * scale_max  out DEVICE float32[n_peers], 4-byte aligned
+ * No output may overlap an input or another output.  Scratch and errors as for
+ * sl_peer_stats (the two share the per-device scratch, so calls of either on
+ * one device must not overlap in time).
+ */
+sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                    int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
+                                    void* stream);
+
+/*
  * sl_peer_stats_noalloc -- sl_peer_stats for callers that cannot allocate
  * device memory: code under graph capture (including a first call), tight
  * serving loops, harnesses that forbid hipMalloc.  Same arguments, checks,

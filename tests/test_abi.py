@@ -319,6 +319,33 @@ def test_peer_stats_argument_checks(lib, name):
     assert fn(None, None, 2, 16, None, CNT, MX, None) == SL_ERR_INVALID_ARG
 
 
+def test_peer_stats_interleaved_argument_checks(lib):
+    """Every call here is rejected (or is a no-op) on the host, before any
+    launch and before the scratch is allocated.  3 peers x 16 chunks: records
+    3 x 16 x 112 bytes from R, scales 3 x 16 x 4 bytes from S."""
+    f = lib.sl_peer_stats_interleaved
+    R = P
+    F, CNT, MX = A * 1200, A * 1300, A * 1400
+    assert f(R, S, 3, -1, F, CNT, MX, None) == SL_ERR_SHAPE
+    assert f(R, S, 3, 1 << 31, F, CNT, MX, None) == SL_ERR_SHAPE
+    assert f(R, S, -1, 16, F, CNT, MX, None) == SL_ERR_TOO_MANY_PEERS
+    assert f(R, S, 129, 16, F, CNT, MX, None) == SL_ERR_TOO_MANY_PEERS
+    assert f(R, S, 0, 16, F, CNT, MX, None) == SL_OK                         # no-op
+    assert f(R, S, 3, 16, F, None, MX, None) == SL_ERR_INVALID_ARG
+    assert f(R, S, 3, 16, F, CNT, None, None) == SL_ERR_INVALID_ARG
+    assert f(R, S, 3, 16, F, CNT + 4, MX, None) == SL_ERR_ALIGN
+    assert f(R, S, 3, 16, F, CNT, MX + 2, None) == SL_ERR_ALIGN
+    assert f(None, S, 3, 16, F, CNT, MX, None) == SL_ERR_INVALID_ARG
+    assert f(R, None, 3, 16, F, CNT, MX, None) == SL_ERR_INVALID_ARG
+    assert f(R + 8, S, 3, 16, F, CNT, MX, None) == SL_ERR_ALIGN
+    assert f(R, S + 2, 3, 16, F, CNT, MX, None) == SL_ERR_ALIGN
+    assert f(R, S, 3, 16, F, MX - 8, MX, None) == SL_ERR_INVALID_ARG         # counts (96 bytes) reach scale_max
+    assert f(R, S, 3, 16, CNT - 8, CNT, MX, None) == SL_ERR_INVALID_ARG      # flags (48 bytes) reach counts
+    assert f(R, S, 3, 16, R + 3 * 16 * 112 - 8, CNT, MX, None) == SL_ERR_INVALID_ARG   # flags reach into the records
+    assert f(R, S, 3, 16, F, S + 16, MX, None) == SL_ERR_INVALID_ARG         # counts on the scales
+    assert f(R, S, 3, 16, F, CNT, S + 3 * 16 * 4 - 4, None) == SL_ERR_INVALID_ARG   # scale_max on the last scale
+
+
 def test_peerset_checks_once_and_rejects_bad_tensors():
     import communication_efficient_distributed_amd as sl
     with pytest.raises(ValueError):

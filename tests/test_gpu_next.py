@@ -411,3 +411,38 @@ def test_validate_chunk_major_records(orc):
                            torch.from_numpy(sc.reshape(C * N)).cuda(), flags)
     torch.cuda.synchronize()
     assert_bitwise(flags.cpu().numpy().reshape(C, N), want, "chunk-major flags")
+
+
+def check_peer_stats_interleaved(sl, orc, payloads, scales, with_flags=True):
+    """sl_peer_stats_interleaved on the peers' records laid out chunk-major,
+    against the oracle's per-peer statistics and flags."""
+    N, C = len(payloads), scales[0].size if payloads else 0
+    rec = np.ascontiguousarray(np.stack(payloads, axis=1)) if N else np.zeros((C, 0, 112), np.uint8)
+    sc = np.ascontiguousarray(np.stack(scales, axis=1)) if N else np.zeros((C, 0), np.float32)
+    counts = torch.full((N, 4), -1, dtype=torch.int64, device="cuda")
+    smax = torch.full((N,), -1.0, dtype=torch.float32, device="cuda")
+    flags = torch.full((N, C), 255, dtype=torch.uint8, device="cuda") if with_flags else None
+    note(f"sl_peer_stats_interleaved {N} peers x {C} records, flags={with_flags}")
+    sl.sl_peer_stats_interleaved(torch.from_numpy(rec).cuda(), torch.from_numpy(sc).cuda(), counts, smax, flags=flags)
+    torch.cuda.synchronize()
+    got_c, got_m = counts.cpu().numpy(), smax.cpu().numpy()
+    for p in range(N):
+        wc, wm = orc.peer_stats(payloads[p], scales[p])
+        assert got_c[p].tolist() == wc.tolist(), f"counts of peer {p}"
+        assert_bitwise(got_m[p:p + 1], np.float32([wm]), f"scale_max of peer {p}")
+        if with_flags:
+            assert_bitwise(flags[p].cpu().numpy(), orc.validate(payloads[p], scales[p])[1], f"flags of peer {p}")
+
+
+def test_peer_stats_chunk_major_records(orc):
+    """sl_peer_stats_interleaved: the same statistics and flags as sl_peer_stats
+    for the peers' records laid out chunk-major (24 peers x 1000 records with
+    planted defects, with and without flags), then one record, ragged counts
+    and the most peers."""
+    sl = require_gpu()
+    payloads, scales = defective_peers(orc, 24, 1000, 17)
+    check_peer_stats_interleaved(sl, orc, payloads, scales, with_flags=True)
+    check_peer_stats_interleaved(sl, orc, payloads, scales, with_flags=False)
+    for N, C in ((1, 1), (3, 63), (128, 257)):
+        p_, s_ = defective_peers(orc, N, C, 100 + N)
+        check_peer_stats_interleaved(sl, orc, p_, s_, with_flags=True)
