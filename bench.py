@@ -474,7 +474,28 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
     stats_il = lambda: sl.sl_peer_stats_interleaved(il_r, il_s, counts, smax, flags=flags_all)
     t = timed(stats_il)
     res["peer_stats_24_peers_chunk_major"] = add_back_to_back(kstats(t, bpp, timed.samples), stats_il, bpp)
-    del il_r, il_s
+    # The rows above re-read one set of records, which then sits in the
+    # last-level cache.  The same passes with records from HBM: four sets
+    # (about 640 MB in each layout), taken in turn.
+    pp_sets = [peers] + [sl.PeerSet([x.clone() for x in peer_p], [x.clone() for x in peer_s]) for _ in range(3)]
+    il_sets = [(il_r, il_s)] + [(il_r.clone(), il_s.clone()) for _ in range(3)]
+    turn = [0]
+
+    def rotate(sets):
+        turn[0] += 1
+        return sets[turn[0] % len(sets)]
+
+    cold = {
+        "validate_24_peers_cold": lambda: sl.sl_validate_payloads(rotate(pp_sets), None, flags_all),
+        "peer_stats_24_peers_cold": lambda: sl.sl_peer_stats(rotate(pp_sets), None, counts, smax, flags=flags_all),
+        "peer_stats_24_peers_chunk_major_cold": lambda: sl.sl_peer_stats_interleaved(*rotate(il_sets), counts, smax,
+                                                                                     flags=flags_all),
+    }
+    for name, fn in cold.items():
+        t = timed(fn)
+        res[name] = add_back_to_back(kstats(t, bpp, timed.samples), fn, bpp)
+        res[name]["record_sets"] = len(pp_sets)
+    del il_r, il_s, il_sets, pp_sets
     res["small_round_1m"] = small_round(sl, delta.device)
     return res
 
@@ -1291,8 +1312,8 @@ def summarize_trace(base, outdir):
     groups = {}
     for d in ds:
         name = _sl_key(d["kernel"])
-        if name.startswith(("validate_kernel", "stats_kernel")):
-            # one lane per record (validate) or a fixed grid per peer (statistics): label by grid
+        if name.startswith(("validate_kernel", "stats_kernel", "stats_interleaved_kernel")):
+            # one lane per record (validate) or a fixed grid (statistics): label by grid
             label = f"{name} [grid {d['grid']} x {d['peers']}]"
         else:
             chunks = _chunks_of(d["kernel"], d["grid"], d["wg"])
@@ -1310,7 +1331,8 @@ def summarize_trace(base, outdir):
              "# command:", f"#   {PROFILE_COMMANDS[len(COUNTER_PASSES)]}", f"#   {PROFILE_COMMANDS[-1]}",
              "# Durations are per dispatch from the kernel trace, all dispatches of the run (setup, warmup,",
              "# timed).  The bench line's own HIP-event means for the same run follow the table.",
-             "# validate/stats rows: grid = lanes along x (validate: one per record) x peers.", "",
+             "# validate/stats rows: grid = lanes along x (validate: one per record) x peers (grid rows);",
+             "# each of these rows holds the calls on one record set re-read and on four sets taken in turn.", "",
              f"{'kernel [shape]':<58}{'calls':>7}{'avg_us':>11}{'min_us':>11}{'max_us':>11}"]
     for label, ds in groups.items():
         lines.append(f"{label:<58}{len(ds):>7}{sum(ds) / len(ds):>11.2f}{min(ds):>11.2f}{max(ds):>11.2f}")

@@ -81,8 +81,17 @@ size_t peer_stats_scratch_bytes();
 // (peer_stats_scratch_bytes() bytes; the counters are zero at load).
 hipError_t peer_stats_static_scratch(void** ptr);
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
-                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream,
-                             int64_t rec_stride = SL_PAYLOAD_BYTES, int64_t sc_stride = 1);
+                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream);
+
+// The same statistics and flags for records laid out chunk-major (chunk c's
+// record from peer p at records + (c * n_peers + p) * 112, its scale at
+// scales[c * n_peers + p]), 1 <= n_peers <= SL_MAX_PEERS.  scratch_ptr: device
+// memory of interleaved_stats_scratch_bytes() bytes, zero before the first
+// call (a completed call leaves it zero); calls that share it must not overlap.
+size_t interleaved_stats_scratch_bytes();
+hipError_t launch_peer_stats_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                         int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
+                                         void* scratch_ptr, hipStream_t stream);
 
 hipError_t launch_compress_weights(const float* theta_pre, const float* theta_post, float* ef,
                                    float beta, uint8_t* payload, float* scales, int64_t n_chunks,

@@ -82,7 +82,8 @@ sl_status stats_scratch(void* stream, void** out) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return SL_ERR_HIP;
     void* p = nullptr;
-    const size_t bytes = sl::peer_stats_scratch_bytes();
+    // sl_peer_stats's part, then sl_peer_stats_interleaved's.
+    const size_t bytes = sl::peer_stats_scratch_bytes() + sl::interleaved_stats_scratch_bytes();
     if (hipMalloc(&p, bytes) != hipSuccess) return SL_ERR_HIP;
     // Zeroed before the first statistics kernel, which runs later on the same
     // stream.
@@ -215,7 +216,6 @@ sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales,
     if (overlap(counts, cbytes, scale_max, mbytes) || overlap(flags, fbytes, counts, cbytes) ||
         overlap(flags, fbytes, scale_max, mbytes))
         return SL_ERR_INVALID_ARG;
-    sl::PeerTable table = {};
     if (n_chunks > 0) {
         if (!records || !scales) return SL_ERR_INVALID_ARG;
         if (!aligned(records, 16) || !aligned(scales, 4)) return SL_ERR_ALIGN;
@@ -226,19 +226,13 @@ sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales,
         for (int b = 0; b < 3; ++b)
             if (overlap(bufs[b], lens[b], records, rbytes) || overlap(bufs[b], lens[b], scales, sbytes))
                 return SL_ERR_INVALID_ARG;
-        // Peer p's records start at its slot of chunk 0 and repeat every
-        // n_peers slots (the kernel's record and scale strides).
-        for (int32_t p = 0; p < n_peers; ++p) {
-            table.payload[p] = records + (size_t)p * SL_PAYLOAD_BYTES;
-            table.scales[p] = scales + p;
-        }
     }
     void* scratch = nullptr;
     const sl_status ss = stats_scratch(stream, &scratch);
     if (ss != SL_OK) return ss;
-    return from_hip(sl::launch_peer_stats(table, n_peers, n_chunks, flags, counts, scale_max, scratch,
-                                          static_cast<hipStream_t>(stream),
-                                          (int64_t)n_peers * SL_PAYLOAD_BYTES, (int64_t)n_peers));
+    return from_hip(sl::launch_peer_stats_interleaved(records, scales, n_peers, n_chunks, flags, counts, scale_max,
+                                                      static_cast<uint8_t*>(scratch) + sl::peer_stats_scratch_bytes(),
+                                                      static_cast<hipStream_t>(stream)));
 }
 
 sl_status sl_peer_stats_noalloc(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,

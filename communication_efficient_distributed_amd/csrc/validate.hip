@@ -127,10 +127,7 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 }
 
 // Grid (G, n_peers).  Workgroup g of peer p takes records g*256 + t +
-// k*G*256; flags (if given) as validate_kernel writes them.  Peer p's record c
-// is at payload[p] + c * rec_stride and its scale at scales[p][c * sc_stride]:
-// strides 112 and 1 for per-peer buffers, n_peers * 112 and n_peers for
-// records laid out chunk-major across peers (payload[p] = records + 112 p).  Each workgroup
+// k*G*256; flags (if given) as validate_kernel writes them.  Each workgroup
 // stores its five partial results in its own slot of the scratch, then counts
 // itself in the peer's arrival counter; the workgroup that arrives last (the
 // G-th) adds up the peer's G slots, writes the totals over
@@ -139,8 +136,7 @@ __device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
 // the arrival order.
 __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, int64_t n_chunks, uint8_t* flags,
                                                              uint64_t* counts, uint32_t* scale_max,
-                                                             uint64_t* slots, uint32_t* arrived,
-                                                             int64_t rec_stride, int64_t sc_stride) {
+                                                             uint64_t* slots, uint32_t* arrived) {
     __shared__ uint64_t part[kStatWaves][kStatValues];
     __shared__ uint32_t last;
     const int p = (int)blockIdx.y;
@@ -150,11 +146,11 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, in
     uint32_t bad = 0, zero = 0, mag = 0, neg = 0, mx = 0;
 #pragma unroll 2
     for (int64_t c = (int64_t)blockIdx.x * kStatThreads + tid; c < n_chunks; c += stride) {
-        const uint8_t* rec = peers.payload[p] + (size_t)c * (size_t)rec_stride;
+        const uint8_t* rec = peers.payload[p] + (size_t)c * SL_PAYLOAD_BYTES;
         uint32_t w[kIndexWords];
         load_indices(rec, w);
         const v4u cw = load_global16(rec + SL_INDEX_BYTES);
-        const float s = peers.scales[p][(size_t)c * (size_t)sc_stride];
+        const float s = peers.scales[p][c];
         const uint32_t f = record_flags(w, s);
         if (flags) flags[(size_t)p * (size_t)n_chunks + (size_t)c] = (uint8_t)f;
         bad += f ? 1u : 0u;
@@ -238,6 +234,140 @@ __global__ __launch_bounds__(kStatThreads) void stats_kernel(PeerTable peers, in
     if (tid == 0) __hip_atomic_store(&arrived[p], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Chunk-major statistics (records r = c * n_peers + p in memory order, as
+// sl_aggregate_interleaved reads them).  A block of cpb = floor(256 / n_peers)
+// whole chunks is cpb * n_peers consecutive records, one per lane, so lane t of
+// a block always meets peer t % n_peers and keeps that peer's partial results
+// in registers; a wavefront's loads cover consecutive records, as in
+// validate_kernel.  Workgroup g takes blocks g, g + G, g + 2G, ..., so the grid
+// reads the buffer front to back.  At the end the workgroup folds its lanes'
+// results per peer in LDS and adds them with agent-scope atomics to copy
+// g % kIlCopies of the per-peer totals in the scratch (integer sums and a
+// maximum: the totals do not depend on the order).  Same-address atomics
+// serialize, so the copies keep the number landing on one address at G /
+// kIlCopies.  The workgroup that arrives last adds up the copies, writes
+// counts / scale_max and zeroes the copies and its arrival counter for the next
+// call.
+// At 24 peers x 57344 records, four rotating sets (records from HBM): 256
+// workgroups with one copy 49 us, 256 with 8 copies 44 us, 512 with 4 or 8
+// copies 39 us, 768 with 8 or 16 copies 42-45 us, 1024 with 16 or 32 copies
+// 44-50 us; each workgroup on its own contiguous range of chunks (256
+// workgroups, one copy) 50 us.  Two to eight records per lane in flight
+// (unrolling) measured the same.
+constexpr int kIlGroups = 512;
+constexpr int kIlCopies = 8;
+constexpr size_t kIlTotalsBytes = (size_t)kIlCopies * SL_MAX_PEERS * 4 * sizeof(uint64_t);
+constexpr size_t kIlMaxBytes = (size_t)kIlCopies * SL_MAX_PEERS * sizeof(uint32_t);
+constexpr size_t kIlScratchBytes = kIlTotalsBytes + kIlMaxBytes + 256;
+
+__global__ __launch_bounds__(kStatThreads) void stats_interleaved_kernel(const uint8_t* records, const float* scales,
+                                                                         int32_t n_peers, int64_t n_chunks,
+                                                                         uint8_t* flags,
+                                                                         uint64_t* counts, uint32_t* scale_max,
+                                                                         uint64_t* totals, uint32_t* maxima,
+                                                                         uint32_t* arrived) {
+    __shared__ uint64_t acc[4][SL_MAX_PEERS];
+    __shared__ uint32_t amax[SL_MAX_PEERS];
+    __shared__ uint32_t last;
+    const int tid = (int)threadIdx.x;
+    const int n = (int)n_peers;
+    const int cpb = kStatThreads / n;  // whole chunks per block
+    const int p = tid % n;
+    const int dc = tid / n;  // this lane's chunk within a block (lanes with dc >= cpb are idle)
+    for (int i = tid; i < n; i += kStatThreads) {
+        acc[0][i] = 0;
+        acc[1][i] = 0;
+        acc[2][i] = 0;
+        acc[3][i] = 0;
+        amax[i] = 0;
+    }
+    uint32_t bad = 0, zero = 0, mag = 0, neg = 0, mx = 0;
+    const int64_t c_step = (int64_t)gridDim.x * cpb;
+    if (dc < cpb) {
+#pragma unroll 2
+        for (int64_t c = (int64_t)blockIdx.x * cpb + dc; c < n_chunks; c += c_step) {
+            const size_t r = (size_t)c * (size_t)n + (size_t)p;
+            const uint8_t* rec = records + r * SL_PAYLOAD_BYTES;
+            uint32_t w[kIndexWords];
+            load_indices(rec, w);
+            const v4u cw = load_global16(rec + SL_INDEX_BYTES);
+            const float s = scales[r];
+            const uint32_t f = record_flags(w, s);
+            if (flags) flags[(size_t)p * (size_t)n_chunks + (size_t)c] = (uint8_t)f;
+            bad += f ? 1u : 0u;
+            zero += s == 0.0f ? 1u : 0u;
+            mag += __popc(cw.x & 0x55555555u) + __popc(cw.y & 0x55555555u) + __popc(cw.z & 0x55555555u) +
+                   __popc(cw.w & 0x55555555u);
+            neg += __popc(cw.x & 0xaaaaaaaau) + __popc(cw.y & 0xaaaaaaaau) + __popc(cw.z & 0xaaaaaaaau) +
+                   __popc(cw.w & 0xaaaaaaaau);
+            const uint32_t key = __float_as_uint(s) & 0x7fffffffu;
+            if ((f & 6u) == 0u && key > mx) mx = key;
+        }
+    }
+    __syncthreads();  // acc and amax are zero
+    if (dc < cpb) {
+        if (bad) __hip_atomic_fetch_add(&acc[0][p], (uint64_t)bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (zero) __hip_atomic_fetch_add(&acc[1][p], (uint64_t)zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (mag) __hip_atomic_fetch_add(&acc[2][p], (uint64_t)mag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (neg) __hip_atomic_fetch_add(&acc[3][p], (uint64_t)neg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (mx) __hip_atomic_fetch_max(&amax[p], mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    // One lane per peer (n_peers <= 128 < 256).  Zero contributions are
+    // skipped; the totals are agent-scope atomics, coherent across the XCDs'
+    // caches, and the wait below holds the arrival until they are done (see
+    // stats_kernel for why no release / acquire is needed).
+    const int cp = (int)(blockIdx.x % kIlCopies);
+    if (tid < n) {
+        uint64_t* tot = totals + (size_t)(cp * SL_MAX_PEERS + tid) * 4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t v = acc[k][tid];
+            if (v) __hip_atomic_fetch_add(&tot[k], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint32_t m = amax[tid];
+        if (m) __hip_atomic_fetch_max(&maxima[cp * SL_MAX_PEERS + tid], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // no reordering by the compiler
+    __builtin_amdgcn_s_waitcnt(kWaitStoresDone);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = before == gridDim.x - 1 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (last == 0u) return;  // the whole workgroup
+    // This runs after every other workgroup has finished, so its latency is
+    // the kernel's tail: all the copies' loads are issued first and waited for
+    // once, then the zeroing stores.  (Zeroing each copy right after loading
+    // it made the compiler wait for every load in turn: 33 round trips, 13-16
+    // us at 24 peers.)
+    if (tid < n) {
+        uint64_t t[4] = {0, 0, 0, 0};
+        uint32_t tm = 0;
+#pragma unroll
+        for (int q = 0; q < kIlCopies; ++q) {
+            const uint64_t* tot = totals + (size_t)(q * SL_MAX_PEERS + tid) * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t[k] += __hip_atomic_load(&tot[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t v = __hip_atomic_load(&maxima[q * SL_MAX_PEERS + tid], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            tm = v > tm ? v : tm;
+        }
+#pragma unroll
+        for (int q = 0; q < kIlCopies; ++q) {
+            uint64_t* tot = totals + (size_t)(q * SL_MAX_PEERS + tid) * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) __hip_atomic_store(&tot[k], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&maxima[q * SL_MAX_PEERS + tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) counts[4 * (size_t)tid + k] = t[k];
+        scale_max[tid] = tm;
+    }
+    if (tid == 0) __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
 
 hipError_t launch_validate(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
@@ -272,8 +402,7 @@ hipError_t peer_stats_static_scratch(void** ptr) {
 
 
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
-                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream,
-                             int64_t rec_stride, int64_t sc_stride) {
+                             int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream) {
     const int64_t per_peer = (kStatGroups + n_peers - 1) / n_peers;
     const int64_t needed = (n_chunks + kStatThreads - 1) / kStatThreads;
     const int64_t gx = needed < 1 ? 1 : needed < per_peer ? needed : per_peer;
@@ -285,9 +414,30 @@ hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_
     uint64_t* slots = reinterpret_cast<uint64_t*>(scratch_ptr);
     uint32_t* arrived = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(scratch_ptr) + kStatSlotBytes);
     PeerTable t = peers;
-    void* args[] = {(void*)&t,      (void*)&n_chunks, (void*)&flags,      (void*)&cnt,      (void*)&mx,
-                    (void*)&slots,  (void*)&arrived,  (void*)&rec_stride, (void*)&sc_stride};
+    void* args[] = {(void*)&t,     (void*)&n_chunks, (void*)&flags, (void*)&cnt,
+                    (void*)&mx,    (void*)&slots,    (void*)&arrived};
     return hipLaunchKernel(reinterpret_cast<const void*>(&stats_kernel), dim3((unsigned)gx, (unsigned)n_peers),
+                           dim3(kStatThreads), args, 0, stream);
+}
+
+size_t interleaved_stats_scratch_bytes() { return kIlScratchBytes; }
+
+hipError_t launch_peer_stats_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
+                                         int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
+                                         void* scratch_ptr, hipStream_t stream) {
+    if (n_peers < 1 || n_peers > SL_MAX_PEERS || n_chunks < 0) return hipErrorInvalidValue;
+    const int64_t cpb = kStatThreads / n_peers;
+    const int64_t blocks = (n_chunks + cpb - 1) / cpb;
+    const int64_t gx = blocks < 1 ? 1 : blocks < kIlGroups ? blocks : kIlGroups;
+    uint64_t* cnt = reinterpret_cast<uint64_t*>(counts);
+    uint32_t* mx = reinterpret_cast<uint32_t*>(scale_max);
+    uint8_t* base = static_cast<uint8_t*>(scratch_ptr);
+    uint64_t* totals = reinterpret_cast<uint64_t*>(base);
+    uint32_t* maxima = reinterpret_cast<uint32_t*>(base + kIlTotalsBytes);
+    uint32_t* arrived = reinterpret_cast<uint32_t*>(base + kIlTotalsBytes + kIlMaxBytes);
+    void* args[] = {(void*)&records, (void*)&scales, (void*)&n_peers, (void*)&n_chunks, (void*)&flags,
+                    (void*)&cnt,     (void*)&mx,     (void*)&totals,  (void*)&maxima,   (void*)&arrived};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&stats_interleaved_kernel), dim3((unsigned)gx),
                            dim3(kStatThreads), args, 0, stream);
 }
 

@@ -283,12 +283,13 @@ sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* cons
  * No output may overlap another output or any payload or scale buffer.
  *
  * One kernel launch.  Its workgroups hand partial results to each other
- * through a 15,872-byte device buffer that the library allocates and zeroes on
- * the first call on each device and keeps until the process ends.  That first
- * call must not be made while its stream is being captured into a graph
- * (SL_ERR_HIP); later calls allocate nothing.  All calls on one device share
- * the buffer, so calls that overlap in time (streams with no ordering between
- * them) race.
+ * through a 15,872-byte part of a device buffer that the library allocates and
+ * zeroes on the first call of sl_peer_stats or sl_peer_stats_interleaved on
+ * each device and keeps until the process ends (52,992 bytes in all).  That
+ * first call must not be made while its stream is being captured into a graph
+ * (SL_ERR_HIP); later calls allocate nothing.  All sl_peer_stats calls on one
+ * device share that part, so calls that overlap in time (streams with no
+ * ordering between them) race.
  */
 sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
                         int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
@@ -311,9 +312,17 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
  * flags      out DEVICE uint8[n_peers][n_chunks] or NULL
  * counts     out DEVICE int64[n_peers][4], 8-byte aligned
  * scale_max  out DEVICE float32[n_peers], 4-byte aligned
- * No output may overlap an input or another output.  Scratch and errors as for
- * sl_peer_stats (the two share the per-device scratch, so calls of either on
- * one device must not overlap in time).
+ * No output may overlap an input or another output.  Errors as for
+ * sl_peer_stats.
+ *
+ * One kernel launch that reads the records in memory order, 256 lanes over
+ * whole chunks, so each lane meets one peer; the workgroups add their per-peer
+ * sums and maxima to eight copies of the totals with device-scope integer
+ * atomics (the totals do not depend on the order), and the last one to finish
+ * writes counts and scale_max and zeroes the copies.  The copies live in the
+ * 37,120-byte second part of sl_peer_stats's device buffer (allocated as
+ * described there), so calls of sl_peer_stats_interleaved on one device must
+ * not overlap in time; they may overlap sl_peer_stats calls.
  */
 sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
                                     int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,

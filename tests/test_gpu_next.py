@@ -446,3 +446,46 @@ def test_peer_stats_chunk_major_records(orc):
     for N, C in ((1, 1), (3, 63), (128, 257)):
         p_, s_ = defective_peers(orc, N, C, 100 + N)
         check_peer_stats_interleaved(sl, orc, p_, s_, with_flags=True)
+
+
+@pytest.mark.parametrize("N,C", [(85, 77), (100, 333), (24, 7687), (1, 70000), (128, 2049)])
+def test_peer_stats_chunk_major_block_edges(orc, N, C):
+    """sl_peer_stats_interleaved where a workgroup's block of whole chunks
+    leaves lanes idle (85 and 100 peers: 255 and 200 of 256 lanes), where a
+    workgroup takes several blocks and the last workgroup a partial one
+    (24 x 7687, 1 x 70000, 128 x 2049), against the oracle."""
+    sl = require_gpu()
+    payloads, scales = defective_peers(orc, N, C, 300 + N)
+    check_peer_stats_interleaved(sl, orc, payloads, scales, with_flags=True)
+
+
+def test_peer_stats_chunk_major_repeated_calls(orc):
+    """Consecutive sl_peer_stats_interleaved calls, each of which must start
+    from zero totals (the previous call leaves them so), with sl_peer_stats
+    (whose part of the same scratch allocation is separate) in between, then a
+    call with no records: zero counts and a +0 scale maximum."""
+    sl = require_gpu()
+    a = defective_peers(orc, 24, 1000, 41)
+    b = defective_peers(orc, 5, 300, 42)
+    check_peer_stats_interleaved(sl, orc, *a, with_flags=True)
+    check_peer_stats_interleaved(sl, orc, *b, with_flags=False)
+    pays = [torch.from_numpy(pl).cuda() for pl in a[0]]
+    scs = [torch.from_numpy(sc).cuda() for sc in a[1]]
+    counts = torch.full((24, 4), -1, dtype=torch.int64, device="cuda")
+    smax = torch.full((24,), -1.0, dtype=torch.float32, device="cuda")
+    note("sl_peer_stats 24 x 1000 between chunk-major calls")
+    sl.sl_peer_stats(pays, scs, counts, smax)
+    torch.cuda.synchronize()
+    for p in range(24):
+        wc, _ = orc.peer_stats(a[0][p], a[1][p])
+        assert counts[p].cpu().tolist() == wc.tolist(), f"sl_peer_stats counts of peer {p}"
+    check_peer_stats_interleaved(sl, orc, *a, with_flags=True)
+    counts = torch.full((3, 4), -1, dtype=torch.int64, device="cuda")
+    smax = torch.full((3,), -1.0, dtype=torch.float32, device="cuda")
+    note("sl_peer_stats_interleaved 3 peers x 0 records")
+    sl.sl_peer_stats_interleaved(torch.empty((0, 3, 112), dtype=torch.uint8, device="cuda"),
+                                 torch.empty((0, 3), dtype=torch.float32, device="cuda"), counts, smax)
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [[0, 0, 0, 0]] * 3
+    assert_bitwise(smax.cpu().numpy(), np.zeros(3, np.float32), "scale_max with no records")
+    check_peer_stats_interleaved(sl, orc, *b, with_flags=True)
