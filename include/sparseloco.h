@@ -282,14 +282,17 @@ sl_status sl_validate_payloads(const uint8_t* const* payloads, const float* cons
  * scale_max out float32[n_peers] (device, 4-byte aligned), overwritten
  * No output may overlap another output or any payload or scale buffer.
  *
- * One kernel launch.  Its workgroups hand partial results to each other
- * through a 15,872-byte part of a device buffer that the library allocates and
- * zeroes on the first call of sl_peer_stats or sl_peer_stats_interleaved on
- * each device and keeps until the process ends (52,992 bytes in all).  That
- * first call must not be made while its stream is being captured into a graph
- * (SL_ERR_HIP); later calls allocate nothing.  All sl_peer_stats calls on one
- * device share that part, so calls that overlap in time (streams with no
- * ordering between them) race.
+ * One kernel launch that takes the peers' records peer after peer, each in
+ * memory order.  Its workgroups add their per-peer sums and maxima to eight
+ * copies of the totals with device-scope integer atomics (the totals do not
+ * depend on the order), and the last one to finish writes counts and
+ * scale_max and zeroes the copies.  The copies live in a 37,120-byte part of a
+ * device buffer that the library allocates and zeroes on the first call of
+ * sl_peer_stats or sl_peer_stats_interleaved on each device and keeps until
+ * the process ends (74,240 bytes in all).  That first call must not be made
+ * while its stream is being captured into a graph (SL_ERR_HIP); later calls
+ * allocate nothing.  All sl_peer_stats calls on one device share that part, so
+ * calls that overlap in time (streams with no ordering between them) race.
  */
 sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scales, int32_t n_peers,
                         int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
@@ -316,13 +319,10 @@ sl_status sl_peer_stats(const uint8_t* const* payloads, const float* const* scal
  * sl_peer_stats.
  *
  * One kernel launch that reads the records in memory order, 256 lanes over
- * whole chunks, so each lane meets one peer; the workgroups add their per-peer
- * sums and maxima to eight copies of the totals with device-scope integer
- * atomics (the totals do not depend on the order), and the last one to finish
- * writes counts and scale_max and zeroes the copies.  The copies live in the
- * 37,120-byte second part of sl_peer_stats's device buffer (allocated as
- * described there), so calls of sl_peer_stats_interleaved on one device must
- * not overlap in time; they may overlap sl_peer_stats calls.
+ * whole chunks, so each lane meets one peer; the totals are formed as in
+ * sl_peer_stats, in the 37,120-byte second part of its device buffer
+ * (allocated as described there), so calls of sl_peer_stats_interleaved on
+ * one device must not overlap in time; they may overlap sl_peer_stats calls.
  */
 sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales, int32_t n_peers,
                                     int64_t n_chunks, uint8_t* flags, int64_t* counts, float* scale_max,
@@ -335,14 +335,14 @@ sl_status sl_peer_stats_interleaved(const uint8_t* records, const float* scales,
  * results and single kernel launch as sl_peer_stats; it calls no hipMalloc,
  * hipFree or other allocating routine.
  *
- * Its scratch is a static device array of 15,872 bytes on every GPU the library
+ * Its scratch is a static device array of 37,120 bytes on every GPU the library
  * runs on, held until the process ends.  Every valid call fits in it
  * (n_peers <= SL_MAX_PEERS, any n_chunks), so no size is refused beyond the
  * checks above.  All calls on one GPU share that GPU's array: calls that
  * overlap in time there (streams with no ordering between them, or with a
- * concurrent sl_peer_stats_noalloc from another thread) race.  Its arrival
- * counters are zero when the library is loaded and every completed call leaves
- * them at zero.  It does not share scratch with sl_peer_stats.
+ * concurrent sl_peer_stats_noalloc from another thread) race.  Its totals and
+ * arrival counter are zero when the library is loaded and every completed call
+ * leaves them at zero.  It does not share scratch with sl_peer_stats.
  * Returns SL_ERR_HIP if the array's device address cannot be found.
  */
 sl_status sl_peer_stats_noalloc(const uint8_t* const* payloads, const float* const* scales,

@@ -154,6 +154,19 @@ def check_peer_stats(sl, orc, payloads, scales, with_flags=True):
     return got_c, got_m
 
 
+@pytest.mark.parametrize("N,C", [(5, 1025), (24, 7687), (128, 2049), (1, 70000), (3, 4096)])
+def test_peer_stats_super_block_edges(orc, N, C):
+    """sl_peer_stats where a peer's last super-block of 1024 records holds one
+    record (5 x 1025, 128 x 2049), where the grid of 512 workgroups takes
+    several super-blocks each and neighbouring super-blocks belong to
+    different peers (24 x 7687, 128 x 2049), one peer spread over 69
+    super-blocks (1 x 70000) and whole super-blocks only (3 x 4096), against
+    the oracle."""
+    sl = require_gpu()
+    payloads, scales = defective_peers(orc, N, C, 500 + N)
+    check_peer_stats(sl, orc, payloads, scales, with_flags=True)
+
+
 def test_peer_stats_against_the_oracle(orc):
     """sl_peer_stats over 24 peers x 1000 records with planted defects,
     crafted all-magnitude chunks, zero scales and an infinite scale; counts,
