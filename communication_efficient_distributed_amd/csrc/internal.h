@@ -72,13 +72,13 @@ hipError_t launch_validate(const PeerTable& peers, int32_t n_peers, int64_t n_ch
                            hipStream_t stream);
 
 // Per-peer statistics (and, if flags is not null, the validation flags) of
-// n_peers peers' n_chunks records in one launch.  counts: int64[n_peers][4],
-// scale_max: float32[n_peers], both overwritten.  scratch_ptr: device memory of
-// peer_stats_scratch_bytes() bytes whose arrival counters are zero (as a
-// completed call leaves them); calls that share a scratch must not overlap.
+// n_peers peers' n_chunks records in one launch, 1 <= n_peers <= SL_MAX_PEERS.
+// counts: int64[n_peers][4], scale_max: float32[n_peers], both overwritten.
+// scratch_ptr: device memory of peer_stats_scratch_bytes() bytes, all zero (as
+// a completed call leaves it); calls that share a scratch must not overlap.
 size_t peer_stats_scratch_bytes();
 // The current device's copy of the library's static statistics scratch
-// (peer_stats_scratch_bytes() bytes; the counters are zero at load).
+// (peer_stats_scratch_bytes() bytes, zero at load).
 hipError_t peer_stats_static_scratch(void** ptr);
 hipError_t launch_peer_stats(const PeerTable& peers, int32_t n_peers, int64_t n_chunks, uint8_t* flags,
                              int64_t* counts, float* scale_max, void* scratch_ptr, hipStream_t stream);
