@@ -22,12 +22,13 @@
 // partial results combine with integer atomics in any order and the totals are
 // the same on every run.
 //
-// Mapping: one lane per record, 64 records per wavefront, one grid row per
-// peer.  A lane loads its record's 96 index bytes (six 16-byte loads; the
-// lanes' records are 112 bytes apart, so every line is fetched once and the
-// later loads hit L2) and unpacks the 64 12-bit fields with compile-time
+// Validation mapping: one lane per record, 64 records per wavefront, one grid
+// row per peer.  A lane loads its record's 96 index bytes (six 16-byte loads;
+// the lanes' records are 112 bytes apart, so every line is fetched once and
+// the later loads hit L2) and unpacks the 64 12-bit fields with compile-time
 // shifts.  (Staging the wavefront's 7 KiB of records through LDS with fully
-// coalesced loads measured no faster.)
+// coalesced loads measured no faster.)  The statistics kernels use the same
+// per-record checks; their mappings are described where they are defined.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
