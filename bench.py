@@ -496,6 +496,28 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
         res[name] = add_back_to_back(kstats(t, bpp, timed.samples), fn, bpp)
         res[name]["record_sets"] = len(pp_sets)
     del il_r, il_s, il_sets, pp_sets
+    # The 24-peer aggregate with records from HBM, the peers' records and
+    # scales packed as a receiver would allocate its receive buffers: one
+    # [N, C, 112] record buffer and one [N, C] scale buffer per set (same
+    # per-peer entry point), four sets taken in turn.
+    C_ = n // CHUNK
+    packed = []
+    for k in range(4):
+        rec = torch.empty((N_PEERS, C_, PAYLOAD), dtype=torch.uint8, device=delta.device)
+        sc = torch.empty((N_PEERS, C_), dtype=torch.float32, device=delta.device)
+        for q in range(N_PEERS):
+            rec[q].copy_(peer_p[q].view(C_, PAYLOAD))
+            sc[q].copy_(peer_s[q])
+        packed.append((rec, sc, sl.PeerSet([rec[q] for q in range(N_PEERS)], [sc[q] for q in range(N_PEERS)])))
+    dense = torch.empty(n, dtype=torch.float32, device=delta.device)
+    agg_p = lambda: sl.sl_aggregate(rotate([x[2] for x in packed]), None, dense)
+    bpa = 4 + N_PEERS * RECORD / CHUNK
+    t = timed(agg_p)
+    res["aggregate_cold_packed"] = add_back_to_back(kstats(t, bpa, timed.samples), agg_p, bpa)
+    res["aggregate_cold_packed"].update({"record_sets": len(packed),
+                                         "note": "sl_aggregate on records from HBM, each set's records in one "
+                                                 "[N, C, 112] buffer and its scales in one [N, C] buffer"})
+    del packed, dense
     res["small_round_1m"] = small_round(sl, delta.device)
     return res
 
