@@ -1104,7 +1104,8 @@ def _label_mlp(dispatches, line):
                     "compress_timed" if timed else "compress")
             elif name == step_agg:
                 label = ("aggregate_timed" if W <= i < W + K else "aggregate") if i < W + K else (
-                    "aggregate_cold" if i < W + K + S + K else None)
+                    "aggregate_cold" if i < W + K + S + K else
+                    "aggregate_cold_packed" if "next_rows" in line else None)
             elif name == "apply_mean_kernel":
                 label = "apply_mean"
             elif name.startswith("aggregate_apply4_kernel"):
@@ -1328,6 +1329,7 @@ def summarize_trace(base, outdir):
     suffix = {"aggregate": ", records cached", "aggregate_cold": ", records from HBM",
               "compress_host_ef": ", ef in host memory", "decoder_one_set": ", one record set re-read",
               "aggregate_cold_interleaved": ", records from HBM, chunk-major",
+              "aggregate_cold_packed": ", records from HBM, packed receive buffers",
               "decoder_two_sets": ", two record sets alternated"}
     timed_of = {"compress_timed": "compress_kernel<false> [8192x28672, timed steps only]",
                 "aggregate_timed": "step aggregate [8192x28672, records cached, timed steps only]"}
