@@ -502,3 +502,57 @@ def test_peer_stats_chunk_major_repeated_calls(orc):
     assert counts.cpu().tolist() == [[0, 0, 0, 0]] * 3
     assert_bitwise(smax.cpu().numpy(), np.zeros(3, np.float32), "scale_max with no records")
     check_peer_stats_interleaved(sl, orc, *b, with_flags=True)
+
+
+@pytest.mark.parametrize("N,C", [(24, 777), (81, 131)])
+def test_repeated_calls_are_bit_identical(orc, N, C):
+    """Every aggregation, validation and statistics entry point, called twice
+    on the same inputs, gives bit-identical outputs; the chunk-major entry
+    points give the same bits as the per-peer ones on the same records.  The
+    aggregates take well-formed records packed by the oracle (the one-chunk
+    kernels with three and with nine record loads per lane), validation and
+    statistics the same peers with planted defects."""
+    sl = require_gpu()
+    n = C * 4096
+
+    def layouts(payloads, scales):
+        pays = [torch.from_numpy(x).cuda() for x in payloads]
+        scs = [torch.from_numpy(x).cuda() for x in scales]
+        rec = torch.stack([p.view(C, 112) for p in pays], dim=1).contiguous()
+        return sl.PeerSet(pays, scs), rec, torch.stack(scs, dim=1).contiguous()
+
+    clean = [datagen.random_entries_bulk(C, 900 + p) for p in range(N)]
+    peers, rec, scm = layouts([orc.pack(i, c) for i, c, _ in clean], [s for _, _, s in clean])
+    bad_peers, bad_rec, bad_scm = layouts(*defective_peers(orc, N, C, 900 + N))
+    theta0 = torch.randn(n, generator=torch.Generator().manual_seed(N)).cuda()
+
+    def outputs():
+        note(f"repeated calls: {N} peers x {C} chunks")
+        out = torch.empty(n, dtype=torch.float32, device="cuda")
+        sl.sl_aggregate(peers, None, out)
+        out_il = torch.empty_like(out)
+        sl.sl_aggregate_interleaved(rec, scm, out_il)
+        th = theta0.clone()
+        sl.sl_aggregate_apply(peers, None, th)
+        th_il = theta0.clone()
+        sl.sl_aggregate_apply_interleaved(rec, scm, th_il)
+        flags = torch.empty((N, C), dtype=torch.uint8, device="cuda")
+        sl.sl_validate_payloads(bad_peers, None, flags)
+        counts = torch.empty((N, 4), dtype=torch.int64, device="cuda")
+        smax = torch.empty(N, dtype=torch.float32, device="cuda")
+        sl.sl_peer_stats(bad_peers, None, counts, smax)
+        counts_il = torch.empty_like(counts)
+        smax_il = torch.empty_like(smax)
+        sl.sl_peer_stats_interleaved(bad_rec, bad_scm, counts_il, smax_il)
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in dict(out=out, out_il=out_il, th=th, th_il=th_il, flags=flags,
+                                                     counts=counts, smax=smax, counts_il=counts_il,
+                                                     smax_il=smax_il).items()}
+
+    a, b = outputs(), outputs()
+    for k in a:
+        assert_bitwise(a[k], b[k], f"{k}, second call")
+    assert_bitwise(a["out"], a["out_il"], "aggregate: per-peer against chunk-major")
+    assert_bitwise(a["th"], a["th_il"], "fused update: per-peer against chunk-major")
+    assert_bitwise(a["counts"], a["counts_il"], "statistics: per-peer against chunk-major")
+    assert_bitwise(a["smax"], a["smax_il"], "scale maxima: per-peer against chunk-major")
