@@ -380,14 +380,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, kstats, reps=20):
+# Calls per next_rows row timed with add_back_to_back(timed(...)): NEXT_WARM
+# warm-up calls and NEXT_REPS timed ones, then one warm-up and NEXT_REPS calls
+# back to back (the trace summary counts dispatches with these).
+NEXT_REPS = 20
+NEXT_WARM = 3
+NEXT_ROW_CALLS = NEXT_WARM + NEXT_REPS + 1 + NEXT_REPS
+
+
+def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, kstats, reps=NEXT_REPS):
     """The entry points beyond the compress + aggregate step, on the same
     workload (not part of `value`): fused aggregate + outer update, compression
     straight from pre/post weights, error feedback in pinned host memory, record
     validation for one peer and for all 24 in one launch."""
     import torch
 
-    def timed(fn, k=reps, warm=3):
+    def timed(fn, k=reps, warm=NEXT_WARM):
         # Each call is timed on its own, queued behind a short spin kernel so
         # that the host-side argument marshalling (pointer tables of 24 peers)
         # is done before the GPU reaches it: the events see the kernel only.
@@ -495,7 +503,32 @@ def next_rows(sl, delta, ef, payload, scales, peer_p, peer_s, theta, n, stream, 
         t = timed(fn)
         res[name] = add_back_to_back(kstats(t, bpp, timed.samples), fn, bpp)
         res[name]["record_sets"] = len(pp_sets)
-    del il_r, il_s, il_sets, pp_sets
+    # A round's receive path on records from HBM: the statistics pass (with the
+    # validation flags) and then the aggregate of the same records, per-peer and
+    # chunk-major.  The second pass may find records the first left cached.
+    dense = torch.empty(n, dtype=torch.float32, device=delta.device)
+
+    def receive(sets, stats_fn, agg_fn):
+        def fn():
+            st = rotate(sets)
+            stats_fn(st)
+            agg_fn(st)
+        return fn
+
+    bpr = bpp + 4 + N_PEERS * RECORD / CHUNK
+    for name, fn in (
+            ("receive_24_peers_cold", receive(
+                pp_sets, lambda st: sl.sl_peer_stats(st, None, counts, smax, flags=flags_all),
+                lambda st: sl.sl_aggregate(st, None, dense))),
+            ("receive_24_peers_chunk_major_cold", receive(
+                il_sets, lambda st: sl.sl_peer_stats_interleaved(*st, counts, smax, flags=flags_all),
+                lambda st: sl.sl_aggregate_interleaved(*st, dense)))):
+        t = timed(fn)
+        res[name] = add_back_to_back(kstats(t, bpr, timed.samples), fn, bpr)
+        res[name].update({"record_sets": len(pp_sets),
+                          "note": "per-peer statistics with validation flags, then the 24-peer aggregate of "
+                                  "the same records; bytes are the two passes' algorithmic bytes"})
+    del il_r, il_s, il_sets, pp_sets, dense
     # The 24-peer aggregate with records from HBM, the peers' records and
     # scales packed as a receiver would allocate its receive buffers: one
     # [N, C, 112] record buffer and one [N, C] scale buffer per set (same
@@ -1103,17 +1136,22 @@ def _label_mlp(dispatches, line):
                 label = "compress_host_ef" if n_step <= i < n_step + n_host else (
                     "compress_timed" if timed else "compress")
             elif name == step_agg:
+                # after the step's calls, next_rows: the per-peer receive path,
+                # then the packed receive buffers
+                j = i - (W + K + S + K)
                 label = ("aggregate_timed" if W <= i < W + K else "aggregate") if i < W + K else (
-                    "aggregate_cold" if i < W + K + S + K else
-                    "aggregate_cold_packed" if "next_rows" in line else None)
+                    "aggregate_cold" if j < 0 else None if "next_rows" not in line else
+                    "receive" if j < NEXT_ROW_CALLS else
+                    "aggregate_cold_packed" if j < 2 * NEXT_ROW_CALLS else None)
             elif name == "apply_mean_kernel":
                 label = "apply_mean"
             elif name.startswith("aggregate_apply4_kernel"):
                 label = "aggregate_apply"
             elif name == "compress_kernel<true>":
                 label = "compress_weights"
-            elif name.startswith("aggregate_interleaved_kernel") and i < n_il:
-                label = "aggregate_cold_interleaved"
+            elif name.startswith("aggregate_interleaved_kernel"):
+                label = "aggregate_cold_interleaved" if i < n_il else (
+                    "receive_chunk_major" if "next_rows" in line and i < n_il + NEXT_ROW_CALLS else None)
         if label:
             out.append((label, d))
     return out
@@ -1330,6 +1368,8 @@ def summarize_trace(base, outdir):
               "compress_host_ef": ", ef in host memory", "decoder_one_set": ", one record set re-read",
               "aggregate_cold_interleaved": ", records from HBM, chunk-major",
               "aggregate_cold_packed": ", records from HBM, packed receive buffers",
+              "receive": ", records from HBM, after the statistics pass",
+              "receive_chunk_major": ", records from HBM, chunk-major, after the statistics pass",
               "decoder_two_sets": ", two record sets alternated"}
     timed_of = {"compress_timed": "compress_kernel<false> [8192x28672, timed steps only]",
                 "aggregate_timed": "step aggregate [8192x28672, records cached, timed steps only]"}
