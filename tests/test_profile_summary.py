@@ -197,3 +197,27 @@ def test_command_line_entry_point(tmp_path):
     assert r.returncode == 0, r.stderr
     assert "compress_mlp_8192x28672_counters.txt" in r.stdout
     assert (out / "compress_mlp_8192x28672_counters.txt").exists()
+
+
+def test_next_row_aggregates_are_labelled_by_call_order():
+    """After the step's aggregates, a bench line with next rows labels the
+    per-peer aggregates of the receive path, then those of the packed receive
+    buffers (NEXT_ROW_CALLS each), and the chunk-major aggregates after the
+    step's as the chunk-major receive path; calls beyond those get no role."""
+    line = bench_line()
+    line["next_rows"] = {}
+    n_row = bench.NEXT_ROW_CALLS
+    agg = [{"kernel": AGG, "grid": AGG_ITEMS, "wg": 64, "peers": 1, "us": 1.0}
+           for _ in range(W + K + S + K + 2 * n_row + 3)]
+    il = [{"kernel": IL31, "grid": AGG_ITEMS, "wg": 64, "peers": 1, "us": 1.0} for _ in range(S + K + n_row + 2)]
+    labels = [lab for lab, _ in bench._label_mlp(agg + il, line)]
+    assert labels.count("aggregate_timed") == K and labels.count("aggregate") == W
+    assert labels.count("aggregate_cold") == S + K
+    assert labels.count("receive") == n_row and labels.count("aggregate_cold_packed") == n_row
+    assert labels.count("aggregate_cold_interleaved") == S + K
+    assert labels.count("receive_chunk_major") == n_row
+    assert len(labels) == len(agg) + len(il) - 3 - 2
+    # without next rows the calls after the step's get no role
+    line.pop("next_rows")
+    labels = [lab for lab, _ in bench._label_mlp(agg + il, line)]
+    assert "receive" not in labels and "aggregate_cold_packed" not in labels and "receive_chunk_major" not in labels
