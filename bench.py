@@ -1195,6 +1195,8 @@ def _kernel_sources(which):
     inc = [os.path.join(ROOT, "include", "sparseloco.h")]
     if which == "compress":
         return [os.path.join(CSRC, "compress.hip")] + csrc + inc
+    if which == "validate":
+        return [os.path.join(CSRC, "validate.hip")] + csrc + inc
     return [os.path.join(CSRC, "aggregate.hip"), os.path.join(CSRC, "record.h")] + csrc + inc
 
 
@@ -1314,7 +1316,8 @@ def summarize_counters(base, outdir):
         ds = [d for d in lines_of["fetch"] if _chunks_of(d["kernel"], d["grid"], d["wg"]) == C and
               _sl_key(d["kernel"]).startswith(("aggregate_run_kernel", "aggregate_kernel<")) and
               _sl_key(d["kernel"]).endswith(("false>", "3>", "2>", "1>"))]
-        taken = sum(1 for lab, _ in labelled if lab in ("aggregate", "aggregate_cold"))
+        taken = sum(1 for lab, _ in labelled if lab in ("aggregate", "aggregate_cold", "receive",
+                                                          "aggregate_cold_packed"))
         ds = ds[taken:]
         per = len(ds) // len(counts) if counts else 0
         for j, Pm in enumerate(sorted(counts)):
@@ -1331,11 +1334,37 @@ def summarize_counters(base, outdir):
     if il_counts:
         n_il = line["kernels"]["aggregate_cold_interleaved"]["record_sets"] + line["steps"] \
             if "aggregate_cold_interleaved" in line["kernels"] else 0
+        n_il += NEXT_ROW_CALLS if "next_rows" in line else 0      # the chunk-major receive path
         mlp_il = [d for d in il_ds if _chunks_of(d["kernel"], d["grid"], d["wg"]) == C][n_il:]
         per = len(mlp_il) // len(il_counts)
         for j, Pm in enumerate(il_counts):
             for d in mlp_il[j * per:(j + 1) * per][3:]:
                 run_sections.append((f"8192 x 28672, {Pm} peers, chunk-major", _sl_key(d["kernel"]), d, n, Pm))
+    # Validation and per-peer statistics of the 24 peers (next rows: calls on one
+    # record set re-read and on four sets taken in turn move the same bytes).
+    stat_roles = (
+        ("validate_kernel, 24 peers in one launch (sl_validate_payloads)",
+         lambda d: _sl_key(d["kernel"]).startswith("validate_kernel") and d["grid"] == P * C),
+        ("stats_kernel, 24 peers (sl_peer_stats)", lambda d: _sl_key(d["kernel"]).startswith("stats_kernel")),
+        ("stats_interleaved_kernel, 24 peers, records chunk-major (sl_peer_stats_interleaved)",
+         lambda d: _sl_key(d["kernel"]).startswith("stats_interleaved_kernel")),
+    )
+    stat_lines = []
+    for title, pick in stat_roles:
+        ds = [d for d in lines_of["fetch"] if pick(d)]
+        if ds:
+            body, _ = _counter_block(ds, by_pass, P * C * RECORD, P * C * 1.0, f_fac, w_fac, P * C)
+            stat_lines += ["", f"[{title}]"] + body
+    if stat_lines:
+        lines = _header(f"validation and per-peer statistics, 8192 x 28672 ({C:,} records per peer), {P} peers", cal)
+        lines += [f"validate_code_sha256_16: {code_digest(_kernel_sources('validate'))}   "
+                  "(validate.hip and the headers it includes, comments and whitespace removed)",
+                  "algorithmic bytes: each record's 112 bytes and its 4-byte scale read, one flag byte written; "
+                  "'per 4096-chunk' below is per record"] + stat_lines
+        path = os.path.join(outdir, "validate_stats_mlp_8192x28672_counters.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        written.append(path)
     if run_sections:
         lines = _header("aggregate kernels with records beyond the last-level cache", cal)
         lines += [f"aggregate_code_sha256_16: {code_digest(_kernel_sources('aggregate'))}   "
