@@ -461,12 +461,14 @@ def test_peer_stats_chunk_major_records(orc):
         check_peer_stats_interleaved(sl, orc, p_, s_, with_flags=True)
 
 
-@pytest.mark.parametrize("N,C", [(85, 77), (100, 333), (24, 7687), (1, 70000), (128, 2049)])
+@pytest.mark.parametrize("N,C", [(85, 77), (100, 333), (24, 7687), (1, 70000), (128, 2049), (24, 57344)])
 def test_peer_stats_chunk_major_block_edges(orc, N, C):
     """sl_peer_stats_interleaved where a workgroup's block of whole chunks
     leaves lanes idle (85 and 100 peers: 255 and 200 of 256 lanes), where a
     workgroup takes several blocks and the last workgroup a partial one
-    (24 x 7687, 1 x 70000, 128 x 2049), against the oracle."""
+    (24 x 7687, 1 x 70000, 128 x 2049), and at the full 8192 x 28672 shape
+    with 24 peers (eleven or twelve blocks per workgroup, as the bench times
+    it), against the oracle."""
     sl = require_gpu()
     payloads, scales = defective_peers(orc, N, C, 300 + N)
     check_peer_stats_interleaved(sl, orc, payloads, scales, with_flags=True)
